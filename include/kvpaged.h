@@ -1,0 +1,177 @@
+/*
+ * kvpaged.h -- C ABI of a paged KV cache and attention over it, for MI355X (gfx950).
+ *
+ * The operation (TensorFold PR #1620, paged K/V for Kolibri-1's full layers, opening
+ * description): the full layers keep K and V in fixed-size pages of one shared pool
+ * ("pages of 512 positions"; the kernel-contract bullet also runs pages of 37 and 64), every
+ * stream leases pages as it grows, new rows are copied into their page slots ("Writes"
+ * bullet), and attention reads keys through a per-stream page table given in the call's
+ * stream order ("Reads" bullet); sliding layers keep rings.  Decode and drafted verify read
+ * through the table, with verify windows of 1..8 causal rows (TensorFold PR #2730: the
+ * pending token plus up to seven drafts), and prompts have their own paged kernels.
+ *
+ * Conventions shared by every call:
+ *   - Every call returns kv_status.  Nothing aborts, throws or synchronises the device.  On a
+ *     non-OK status no state changed and no kernel was launched (except KV_E_DEVICE, which
+ *     reports a failed launch); kv_last_error() gives the text, per calling thread.
+ *   - All device buffers (pages, queries, outputs, new rows, tables, lengths, workspace) are
+ *     allocated and owned by the caller and must outlive the calls that use them.  The library
+ *     owns only host metadata (the pool's free list and per-stream lease lists) and allocates
+ *     no device memory.
+ *   - `hip_stream` is a hipStream_t (NULL = the legacy default stream).  Device work is
+ *     enqueued on it asynchronously, in the order of the calls.
+ *   - bf16 means IEEE binary32 truncated to its high 16 bits (raw uint16 storage).
+ *   - Table contents and device lengths are trusted on the hot path; with the environment
+ *     variable KVP_CHECK=1 every call copies them to the host first (synchronously) and refuses
+ *     bad ones with KV_E_ARG.  Without it, a page id outside [0, num_pages) is never
+ *     dereferenced (its rows read as zeros and are not written), so a bad table gives a wrong
+ *     result but touches no memory outside the pool.
+ */
+#ifndef KVPAGED_H
+#define KVPAGED_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KVPAGED_ABI_VERSION 1
+
+typedef enum kv_status {
+    KV_OK = 0,
+    KV_E_ARG = -1,        /* a null pointer, a negative or inconsistent size, a bad stream id */
+    KV_E_SHAPE = -2,      /* a shape this build has no kernel for (head_dim, GQA group, rows) */
+    KV_E_NO_PAGES = -3,   /* a lease asked for more pages than are free (nothing was leased) */
+    KV_E_WORKSPACE = -4,  /* the workspace passed is smaller than paged_attn_workspace_size() */
+    KV_E_DEVICE = -5      /* the HIP runtime reported an error for a launch */
+} kv_status;
+
+/* Opaque pool handle: host metadata only (geometry, free list, leases). */
+typedef struct kv_pool kv_pool;
+
+/* Pool geometry and storage.  K and V pages are caller-owned device arrays of bf16 laid out
+ * [num_pages][num_kv_heads][page_size][head_dim]: one KV head's rows inside a page are
+ * contiguous, and a row is head_dim contiguous values. */
+typedef struct kv_pool_desc {
+    int32_t num_pages;       /* > 0 */
+    int32_t page_size;       /* P >= 1 positions per page (512 by default; any value works) */
+    int32_t num_kv_heads;    /* Hkv >= 1 */
+    int32_t head_dim;        /* D >= 8, a multiple of 8 (attention needs 128 or 512) */
+    int32_t max_streams;     /* number of stream ids [0, max_streams) that may lease */
+    void *k_pages;           /* device, bf16 [num_pages][Hkv][P][D] */
+    void *v_pages;           /* device, bf16 [num_pages][Hkv][P][D] */
+    const int32_t *free_order; /* host, optional [num_pages]: a permutation of the page ids
+                                  giving the order pages are handed out; NULL = 0,1,2,...
+                                  Copied at creation. */
+} kv_pool_desc;
+
+/* One call's streams.  Stream i of the call uses row i of the page table and seq_len[i]. */
+typedef struct kv_layout {
+    int32_t num_streams;       /* S >= 1 */
+    int32_t rows;              /* R >= 1: new rows (kv_rows_put) or query rows per stream */
+    const int32_t *page_table; /* device int32 [S][table_stride]: entry i is the physical page
+                                  of the stream's logical page i (full layers) or ring slot i
+                                  (ring layers) */
+    int32_t table_stride;      /* >= the entries a stream uses (ceil(L/P), or ring_pages) */
+    const int32_t *seq_len;    /* device int32 [S]: the stream's length L after this call's rows;
+                                  the call's rows sit at positions L-R .. L-1, so R <= L */
+    int32_t max_seq_len;       /* host: an upper bound of seq_len over the call (sizes grids and
+                                  the workspace; a larger device length is a caller error) */
+    int32_t ring_pages;        /* 0: full layer, position j lives in page table[j / P];
+                                  n > 0: ring of n pages, position j lives in
+                                  table[(j / P) % n], so only the newest n*P positions exist */
+} kv_layout;
+
+/* Attention arguments. */
+typedef struct kv_attn_args {
+    const void *q;           /* device bf16 [S][R][Hq][D] */
+    void *out;               /* device bf16 [S][R][Hq][D], written in full */
+    int32_t num_q_heads;     /* Hq, a multiple of Hkv; query head h reads KV head h / (Hq/Hkv) */
+    float scale;             /* score scale; 0 means 1/sqrt(D) */
+    int32_t window;          /* 0: full causal; W > 0: row at position p sees keys p-W+1 .. p */
+    void *workspace;         /* device scratch, >= paged_attn_workspace_size() bytes, 256-byte
+                                aligned; its contents on entry do not matter */
+    size_t workspace_bytes;
+} kv_attn_args;
+
+/* Create a pool over caller-owned pages (TensorFold PR #1620, opening description: "Arena,
+ * plan and leasing" -- the arena is the caller's pair of page arrays, leasing is below).
+ * Errors: KV_E_ARG for a null desc/out/page pointer, a non-positive size, D not a multiple of
+ * 8, or a free_order that is not a permutation of [0, num_pages). */
+kv_status kv_pool_create(const kv_pool_desc *desc, kv_pool **out);
+
+/* Destroy the host metadata (never the caller's pages).  NULL is accepted. */
+kv_status kv_pool_destroy(kv_pool *pool);
+
+/* Lease n pages to a stream as it grows (TensorFold PR #1620, opening description: "every
+ * stream leasing as it grows").  Pages come off the front of the free queue in queue order,
+ * are appended to the stream's lease list and are written to page_ids_out (host [n]).
+ * All or nothing: with fewer than n free pages it returns KV_E_NO_PAGES and changes nothing.
+ * KV_E_ARG for a bad stream id, n < 0, or a null output with n > 0.  Thread-safe per pool. */
+kv_status kv_page_lease(kv_pool *pool, int32_t stream, int32_t n, int32_t *page_ids_out);
+
+/* Return all of a stream's pages to the back of the free queue, in the order they were leased
+ * (released pages are reused by later leases: the model test's "reused pages").  KV_E_ARG for
+ * a bad stream id.  The pages' contents are left as they are. */
+kv_status kv_page_release(kv_pool *pool, int32_t stream);
+
+/* Number of free pages. */
+kv_status kv_pool_free_count(const kv_pool *pool, int32_t *out);
+
+/* Copy up to `cap` of a stream's leased page ids, in lease order, to ids_out (host); *n_out
+ * receives the stream's total count (which may exceed cap). */
+kv_status kv_stream_pages(const kv_pool *pool, int32_t stream, int32_t *ids_out, int32_t cap,
+                          int32_t *n_out);
+
+/* Write each stream's R new K and V rows into their page slots (TensorFold PR #1620, opening
+ * description, "Writes" bullet: the rows kernel's new K/V rows are copied into the pages).
+ * k_new, v_new: device bf16 [S][R][Hkv][D].  Row r of stream s goes to position
+ * seq_len[s] - R + r, i.e. page table[s][pos / P] (or ring slot (pos / P) % ring_pages) at
+ * slot pos % P, for every KV head.  Rows at negative positions are skipped.  Every other byte
+ * of the pool is left untouched.  Errors: KV_E_ARG (null pointers, bad sizes). */
+kv_status kv_rows_put(const kv_pool *pool, const kv_layout *lay, const void *k_new,
+                      const void *v_new, void *hip_stream);
+
+/* Bytes of workspace that a decode/verify/prefill call with these arguments needs (a
+ * function of S, R, Hq, D, the GQA group, max_seq_len and the window only). */
+kv_status paged_attn_workspace_size(const kv_pool *pool, const kv_layout *lay,
+                                    const kv_attn_args *a, size_t *bytes);
+
+/* Paged GQA attention for one decode row per stream (R == 1) (TensorFold PR #1620, opening
+ * description, "Reads" bullet: decode reads keys from a page table).  For each stream s and
+ * query head h: out = softmax(scale * q K^T) V over the keys the row sees (all positions
+ * 0..L-1, or the newest `window`), K and V read through the stream's page table.  Computed
+ * with fp32 accumulation; the output is rounded to bf16 (nearest even).  Results depend only
+ * on the logical cache, never on which physical pages hold it (bit for bit).
+ * Errors: KV_E_ARG (R != 1, null pointers, Hq not a multiple of Hkv), KV_E_SHAPE (no kernel
+ * for this head_dim or group), KV_E_WORKSPACE (too small). */
+kv_status paged_attn_decode(const kv_pool *pool, const kv_layout *lay, const kv_attn_args *a,
+                            void *hip_stream);
+
+/* The same for a speculative verify window of 1 <= R <= 8 causal rows per stream (TensorFold
+ * PR #2730: the pending token plus up to seven drafts; "the window kernels already take any row
+ * count").  Row r sits at position L-R+r and sees keys up to and including itself.
+ * Errors as for decode, with KV_E_ARG for R outside 1..8. */
+kv_status paged_attn_verify(const kv_pool *pool, const kv_layout *lay, const kv_attn_args *a,
+                            void *hip_stream);
+
+/* The same for a prompt chunk of any R >= 1 causal rows per stream (TensorFold PR #1620,
+ * opening description, "Reads" bullet: prompts go through paged prompt kernels).  A prompt is
+ * processed chunk by chunk: kv_rows_put the chunk's rows, then this call with R = chunk rows.
+ * Errors as for decode, with KV_E_ARG for R < 1. */
+kv_status paged_attn_prefill(const kv_pool *pool, const kv_layout *lay, const kv_attn_args *a,
+                             void *hip_stream);
+
+/* Text of the calling thread's last non-OK status ("" if none). */
+const char *kv_last_error(void);
+
+/* KVPAGED_ABI_VERSION of the built library. */
+int32_t kv_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVPAGED_H */

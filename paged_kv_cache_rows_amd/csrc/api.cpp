@@ -1,0 +1,371 @@
+// Host side of the C ABI declared in include/kvpaged.h: pool and lease bookkeeping, argument
+// checks done before any launch, and dispatch to the gfx950 kernels.
+#include "../../include/kvpaged.h"
+#include "internal.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <deque>
+#include <mutex>
+#include <string>
+#include <vector>
+
+struct kv_pool {
+    int32_t num_pages, page_size, num_kv_heads, head_dim, max_streams;
+    uint16_t *k_pages;
+    uint16_t *v_pages;
+    mutable std::mutex mu;
+    std::deque<int32_t> free_q;
+    std::vector<std::vector<int32_t>> leased;
+};
+
+namespace {
+
+thread_local std::string g_last_error;
+
+kv_status fail(kv_status st, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return st;
+}
+
+kv_status ok() { return KV_OK; }
+
+bool check_enabled() {
+    const char *e = getenv("KVP_CHECK");
+    return e && e[0] && e[0] != '0';
+}
+
+int ceil_div(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
+
+kv_status check_layout(const kv_pool *pool, const kv_layout *lay, const char *who) {
+    if (!pool) return fail(KV_E_ARG, "%s: pool is null", who);
+    if (!lay) return fail(KV_E_ARG, "%s: layout is null", who);
+    if (lay->num_streams < 1) return fail(KV_E_ARG, "%s: num_streams %d < 1", who, lay->num_streams);
+    if (lay->rows < 1) return fail(KV_E_ARG, "%s: rows %d < 1", who, lay->rows);
+    if (!lay->page_table || !lay->seq_len) return fail(KV_E_ARG, "%s: page_table or seq_len is null", who);
+    if (lay->max_seq_len < lay->rows)
+        return fail(KV_E_ARG, "%s: max_seq_len %d < rows %d", who, lay->max_seq_len, lay->rows);
+    if (lay->ring_pages < 0) return fail(KV_E_ARG, "%s: ring_pages %d < 0", who, lay->ring_pages);
+    const int need = lay->ring_pages ? lay->ring_pages : ceil_div(lay->max_seq_len, pool->page_size);
+    if (lay->table_stride < need)
+        return fail(KV_E_ARG, "%s: table_stride %d < %d entries needed for max_seq_len %d", who,
+                    lay->table_stride, need, lay->max_seq_len);
+    if ((int64_t)lay->num_streams * lay->rows > (int64_t)INT32_MAX / 4)
+        return fail(KV_E_ARG, "%s: too many rows", who);
+    return ok();
+}
+
+// Optional host validation of the device lengths and tables (KVP_CHECK=1).
+// ring_span: how many consecutive positions one call needs the ring to hold (rows for a row
+// write, window + rows - 1 for attention); ignored for full layers.
+kv_status deep_check(const kv_pool *pool, const kv_layout *lay, int64_t ring_span, hipStream_t st, const char *who) {
+    if (!check_enabled()) return ok();
+    const int S = lay->num_streams;
+    std::vector<int32_t> L(S), tab((size_t)S * lay->table_stride);
+    if (hipMemcpyAsync(L.data(), lay->seq_len, sizeof(int32_t) * S, hipMemcpyDeviceToHost, st) != hipSuccess ||
+        hipMemcpyAsync(tab.data(), lay->page_table, sizeof(int32_t) * tab.size(), hipMemcpyDeviceToHost, st) != hipSuccess ||
+        hipStreamSynchronize(st) != hipSuccess)
+        return fail(KV_E_DEVICE, "%s: KVP_CHECK copy failed", who);
+    for (int s = 0; s < S; ++s) {
+        if (L[s] < lay->rows || L[s] > lay->max_seq_len)
+            return fail(KV_E_ARG, "%s: stream %d has seq_len %d outside [rows %d, max_seq_len %d]", who, s, L[s],
+                        lay->rows, lay->max_seq_len);
+        int n;
+        if (lay->ring_pages) {
+            n = lay->ring_pages;
+            const int64_t cap = (int64_t)lay->ring_pages * pool->page_size;
+            if (ring_span > cap)
+                return fail(KV_E_ARG, "%s: a ring of %lld positions cannot hold the %lld a call needs", who,
+                            (long long)cap, (long long)ring_span);
+        } else {
+            n = ceil_div(L[s], pool->page_size);
+        }
+        for (int i = 0; i < n; ++i) {
+            const int32_t pg = tab[(size_t)s * lay->table_stride + i];
+            if (pg < 0 || pg >= pool->num_pages)
+                return fail(KV_E_ARG, "%s: stream %d table entry %d = %d outside [0, %d)", who, s, i, pg,
+                            pool->num_pages);
+        }
+    }
+    return ok();
+}
+
+struct Plan {
+    bool mfma;
+    int D, G, Hkv, Hq, S, R, chunk, n_splits, tiles;
+};
+
+int splits_for(int max_seq_len, int rows, int window, int chunk) {
+    int n = ceil_div(max_seq_len, chunk);
+    if (window > 0) {
+        const int span = ceil_div((int64_t)window + rows - 1, chunk) + 1;
+        if (span < n) n = span;
+    }
+    return n < 1 ? 1 : n;
+}
+
+kv_status make_plan(const kv_pool *pool, const kv_layout *lay, const kv_attn_args *a, Plan *p, const char *who) {
+    kv_status st = check_layout(pool, lay, who);
+    if (st != KV_OK) return st;
+    if (!a) return fail(KV_E_ARG, "%s: args is null", who);
+    if (a->num_q_heads < 1 || a->num_q_heads % pool->num_kv_heads != 0)
+        return fail(KV_E_ARG, "%s: num_q_heads %d is not a positive multiple of num_kv_heads %d", who,
+                    a->num_q_heads, pool->num_kv_heads);
+    if (a->window < 0) return fail(KV_E_ARG, "%s: window %d < 0", who, a->window);
+    if (!(a->scale >= 0.f) || std::isinf(a->scale)) return fail(KV_E_ARG, "%s: scale must be finite and >= 0", who);
+    if (lay->ring_pages && a->window <= 0)
+        return fail(KV_E_ARG, "%s: a ring layer needs a sliding window", who);
+    if (lay->ring_pages && (int64_t)a->window + lay->rows - 1 > (int64_t)lay->ring_pages * pool->page_size)
+        return fail(KV_E_ARG, "%s: ring of %d pages x %d cannot hold window %d plus %d rows", who, lay->ring_pages,
+                    pool->page_size, a->window, lay->rows);
+    p->D = pool->head_dim;
+    p->Hkv = pool->num_kv_heads;
+    p->Hq = a->num_q_heads;
+    p->G = p->Hq / p->Hkv;
+    p->S = lay->num_streams;
+    p->R = lay->rows;
+    const int nq = p->R * p->G;
+    p->mfma = nq >= 16;
+    if (p->mfma) {
+        if (!kvp::mfma_supported(p->D, p->G, p->R))
+            return fail(KV_E_SHAPE, "%s: no MFMA kernel for head_dim %d, group %d, rows %d", who, p->D, p->G, p->R);
+        p->chunk = kvp::mfma_chunk(p->D);
+        p->tiles = kvp::mfma_query_tiles(p->D, p->G, p->R);
+    } else {
+        if (!kvp::valu_supported(p->D, p->G, nq))
+            return fail(KV_E_SHAPE, "%s: no VALU kernel for head_dim %d, group %d, rows %d", who, p->D, p->G, p->R);
+        p->chunk = kvp::valu_chunk(p->D);
+        p->tiles = 1;
+    }
+    p->n_splits = splits_for(lay->max_seq_len, p->R, a->window, p->chunk);
+    return ok();
+}
+
+size_t workspace_bytes(const Plan &p) {
+    return (size_t)p.S * p.R * p.Hq * p.n_splits * (p.D + 2) * sizeof(float);
+}
+
+kv_status run_attention(const kv_pool *pool, const kv_layout *lay, const kv_attn_args *a, void *hip_stream,
+                        const char *who) {
+    Plan p;
+    kv_status st = make_plan(pool, lay, a, &p, who);
+    if (st != KV_OK) return st;
+    if (!a->q || !a->out) return fail(KV_E_ARG, "%s: q or out is null", who);
+    const size_t need = workspace_bytes(p);
+    if (!a->workspace || a->workspace_bytes < need)
+        return fail(KV_E_WORKSPACE, "%s: workspace of %zu bytes, %zu needed", who, a->workspace_bytes, need);
+    if (reinterpret_cast<uintptr_t>(a->workspace) % 256 != 0)
+        return fail(KV_E_ARG, "%s: workspace is not 256-byte aligned", who);
+    hipStream_t hs = reinterpret_cast<hipStream_t>(hip_stream);
+    st = deep_check(pool, lay, (int64_t)a->window + p.R - 1, hs, who);
+    if (st != KV_OK) return st;
+
+    kvp::PartArgs pa;
+    pa.k_pages = pool->k_pages;
+    pa.v_pages = pool->v_pages;
+    pa.table = lay->page_table;
+    pa.seq_len = lay->seq_len;
+    pa.q = static_cast<const uint16_t *>(a->q);
+    pa.ws_acc = static_cast<float *>(a->workspace);
+    pa.ws_ml = pa.ws_acc + (size_t)p.S * p.R * p.Hq * p.n_splits * p.D;
+    pa.num_pages = pool->num_pages;
+    pa.P = pool->page_size;
+    pa.Hkv = p.Hkv;
+    pa.stride = lay->table_stride;
+    pa.ring_pages = lay->ring_pages;
+    pa.R = p.R;
+    pa.Hq = p.Hq;
+    pa.window = a->window;
+    pa.n_splits = p.n_splits;
+    const float scale = a->scale > 0.f ? a->scale : 1.0f / std::sqrt((float)p.D);
+    pa.scale_log2 = scale * 1.4426950408889634f;
+
+    hipError_t e = p.mfma ? kvp::launch_part_mfma(p.D, p.G, pa, p.S, hs)
+                          : kvp::launch_part_valu(p.D, p.G, p.R * p.G, pa, p.S, hs);
+    if (e != hipSuccess) return fail(KV_E_DEVICE, "%s: part kernel launch failed: %s", who, hipGetErrorString(e));
+
+    kvp::MergeArgs ma;
+    ma.ws_acc = pa.ws_acc;
+    ma.ws_ml = pa.ws_ml;
+    ma.seq_len = lay->seq_len;
+    ma.out = static_cast<uint16_t *>(a->out);
+    ma.S = p.S;
+    ma.R = p.R;
+    ma.Hq = p.Hq;
+    ma.D = p.D;
+    ma.window = a->window;
+    ma.n_splits = p.n_splits;
+    ma.chunk = p.chunk;
+    e = kvp::launch_merge(ma, hs);
+    if (e != hipSuccess) return fail(KV_E_DEVICE, "%s: merge launch failed: %s", who, hipGetErrorString(e));
+    return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+kv_status kv_pool_create(const kv_pool_desc *d, kv_pool **out) {
+    if (!d || !out) return fail(KV_E_ARG, "kv_pool_create: desc or out is null");
+    if (d->num_pages < 1 || d->page_size < 1 || d->num_kv_heads < 1 || d->head_dim < 8 || d->max_streams < 1)
+        return fail(KV_E_ARG, "kv_pool_create: sizes must be positive (num_pages %d, page_size %d, kv_heads %d, "
+                    "head_dim %d, max_streams %d)", d->num_pages, d->page_size, d->num_kv_heads, d->head_dim,
+                    d->max_streams);
+    if (d->head_dim % 8 != 0) return fail(KV_E_ARG, "kv_pool_create: head_dim %d is not a multiple of 8", d->head_dim);
+    if (!d->k_pages || !d->v_pages) return fail(KV_E_ARG, "kv_pool_create: k_pages or v_pages is null");
+    if ((reinterpret_cast<uintptr_t>(d->k_pages) | reinterpret_cast<uintptr_t>(d->v_pages)) % 16 != 0)
+        return fail(KV_E_ARG, "kv_pool_create: page arrays must be 16-byte aligned");
+    std::vector<int32_t> order(d->num_pages);
+    if (d->free_order) {
+        std::vector<char> seen(d->num_pages, 0);
+        for (int i = 0; i < d->num_pages; ++i) {
+            const int32_t id = d->free_order[i];
+            if (id < 0 || id >= d->num_pages || seen[id])
+                return fail(KV_E_ARG, "kv_pool_create: free_order is not a permutation of [0, %d)", d->num_pages);
+            seen[id] = 1;
+            order[i] = id;
+        }
+    } else {
+        for (int i = 0; i < d->num_pages; ++i) order[i] = i;
+    }
+    kv_pool *p = new (std::nothrow) kv_pool;
+    if (!p) return fail(KV_E_ARG, "kv_pool_create: out of host memory");
+    p->num_pages = d->num_pages;
+    p->page_size = d->page_size;
+    p->num_kv_heads = d->num_kv_heads;
+    p->head_dim = d->head_dim;
+    p->max_streams = d->max_streams;
+    p->k_pages = static_cast<uint16_t *>(d->k_pages);
+    p->v_pages = static_cast<uint16_t *>(d->v_pages);
+    p->free_q.assign(order.begin(), order.end());
+    p->leased.assign(d->max_streams, {});
+    *out = p;
+    return ok();
+}
+
+kv_status kv_pool_destroy(kv_pool *pool) {
+    delete pool;
+    return ok();
+}
+
+kv_status kv_page_lease(kv_pool *pool, int32_t stream, int32_t n, int32_t *ids) {
+    if (!pool) return fail(KV_E_ARG, "kv_page_lease: pool is null");
+    std::lock_guard<std::mutex> lk(pool->mu);
+    if (stream < 0 || stream >= pool->max_streams)
+        return fail(KV_E_ARG, "kv_page_lease: stream %d outside [0, %d)", stream, pool->max_streams);
+    if (n < 0) return fail(KV_E_ARG, "kv_page_lease: n %d < 0", n);
+    if (n > 0 && !ids) return fail(KV_E_ARG, "kv_page_lease: page_ids_out is null");
+    if ((size_t)n > pool->free_q.size())
+        return fail(KV_E_NO_PAGES, "kv_page_lease: %d pages asked, %zu free", n, pool->free_q.size());
+    auto &lst = pool->leased[stream];
+    for (int i = 0; i < n; ++i) {
+        ids[i] = pool->free_q.front();
+        pool->free_q.pop_front();
+        lst.push_back(ids[i]);
+    }
+    return ok();
+}
+
+kv_status kv_page_release(kv_pool *pool, int32_t stream) {
+    if (!pool) return fail(KV_E_ARG, "kv_page_release: pool is null");
+    std::lock_guard<std::mutex> lk(pool->mu);
+    if (stream < 0 || stream >= pool->max_streams)
+        return fail(KV_E_ARG, "kv_page_release: stream %d outside [0, %d)", stream, pool->max_streams);
+    auto &lst = pool->leased[stream];
+    for (int32_t id : lst) pool->free_q.push_back(id);
+    lst.clear();
+    return ok();
+}
+
+kv_status kv_pool_free_count(const kv_pool *pool, int32_t *out) {
+    if (!pool || !out) return fail(KV_E_ARG, "kv_pool_free_count: null argument");
+    std::lock_guard<std::mutex> lk(pool->mu);
+    *out = (int32_t)pool->free_q.size();
+    return ok();
+}
+
+kv_status kv_stream_pages(const kv_pool *pool, int32_t stream, int32_t *ids_out, int32_t cap, int32_t *n_out) {
+    if (!pool || !n_out) return fail(KV_E_ARG, "kv_stream_pages: null argument");
+    std::lock_guard<std::mutex> lk(pool->mu);
+    if (stream < 0 || stream >= pool->max_streams)
+        return fail(KV_E_ARG, "kv_stream_pages: stream %d outside [0, %d)", stream, pool->max_streams);
+    if (cap < 0 || (cap > 0 && !ids_out)) return fail(KV_E_ARG, "kv_stream_pages: bad output buffer");
+    const auto &lst = pool->leased[stream];
+    const int n = (int)lst.size();
+    for (int i = 0; i < n && i < cap; ++i) ids_out[i] = lst[i];
+    *n_out = n;
+    return ok();
+}
+
+kv_status kv_rows_put(const kv_pool *pool, const kv_layout *lay, const void *k_new, const void *v_new,
+                      void *hip_stream) {
+    kv_status st = check_layout(pool, lay, "kv_rows_put");
+    if (st != KV_OK) return st;
+    if (!k_new || !v_new) return fail(KV_E_ARG, "kv_rows_put: k_new or v_new is null");
+    hipStream_t hs = reinterpret_cast<hipStream_t>(hip_stream);
+    if (lay->ring_pages && (int64_t)lay->rows > (int64_t)lay->ring_pages * pool->page_size)
+        return fail(KV_E_ARG, "kv_rows_put: %d rows overrun a ring of %d x %d positions", lay->rows,
+                    lay->ring_pages, pool->page_size);
+    st = deep_check(pool, lay, lay->rows, hs, "kv_rows_put");
+    if (st != KV_OK) return st;
+    kvp::RowsArgs ra;
+    ra.k_pages = pool->k_pages;
+    ra.v_pages = pool->v_pages;
+    ra.k_new = static_cast<const uint16_t *>(k_new);
+    ra.v_new = static_cast<const uint16_t *>(v_new);
+    ra.table = lay->page_table;
+    ra.seq_len = lay->seq_len;
+    ra.num_pages = pool->num_pages;
+    ra.P = pool->page_size;
+    ra.Hkv = pool->num_kv_heads;
+    ra.D = pool->head_dim;
+    ra.S = lay->num_streams;
+    ra.R = lay->rows;
+    ra.stride = lay->table_stride;
+    ra.ring_pages = lay->ring_pages;
+    const hipError_t e = kvp::launch_rows_put(ra, hs);
+    if (e != hipSuccess) return fail(KV_E_DEVICE, "kv_rows_put: launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+kv_status paged_attn_workspace_size(const kv_pool *pool, const kv_layout *lay, const kv_attn_args *a,
+                                    size_t *bytes) {
+    if (!bytes) return fail(KV_E_ARG, "paged_attn_workspace_size: bytes is null");
+    Plan p;
+    kv_status st = make_plan(pool, lay, a, &p, "paged_attn_workspace_size");
+    if (st != KV_OK) return st;
+    *bytes = workspace_bytes(p);
+    return ok();
+}
+
+kv_status paged_attn_decode(const kv_pool *pool, const kv_layout *lay, const kv_attn_args *a, void *hip_stream) {
+    if (lay && lay->rows != 1) return fail(KV_E_ARG, "paged_attn_decode: rows %d != 1", lay->rows);
+    return run_attention(pool, lay, a, hip_stream, "paged_attn_decode");
+}
+
+kv_status paged_attn_verify(const kv_pool *pool, const kv_layout *lay, const kv_attn_args *a, void *hip_stream) {
+    if (lay && (lay->rows < 1 || lay->rows > 8))
+        return fail(KV_E_ARG, "paged_attn_verify: rows %d outside 1..8", lay->rows);
+    return run_attention(pool, lay, a, hip_stream, "paged_attn_verify");
+}
+
+kv_status paged_attn_prefill(const kv_pool *pool, const kv_layout *lay, const kv_attn_args *a, void *hip_stream) {
+    if (lay && lay->rows < 1) return fail(KV_E_ARG, "paged_attn_prefill: rows %d < 1", lay->rows);
+    return run_attention(pool, lay, a, hip_stream, "paged_attn_prefill");
+}
+
+const char *kv_last_error(void) { return g_last_error.c_str(); }
+
+int32_t kv_abi_version(void) { return KVPAGED_ABI_VERSION; }
+
+}  // extern "C"

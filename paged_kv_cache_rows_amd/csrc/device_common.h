@@ -1,0 +1,78 @@
+// Device helpers shared by the gfx950 kernels: bf16 packing, the bf16 dot2 instruction and
+// wave64 reductions built on DPP row operations plus lane reads.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kvp {
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// c + a.lo * b.lo + a.hi * b.hi, bf16 inputs, fp32 accumulate (v_dot2c_f32_bf16).
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                           __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
+// Two fp32 values rounded to bf16 (nearest even) and packed lo | hi << 16.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    bf16x2_t v;
+    v[0] = (__bf16)lo;
+    v[1] = (__bf16)hi;
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ uint16_t to_bf16_bits(float x) {
+    __bf16 b = (__bf16)x;
+    return __builtin_bit_cast(uint16_t, b);
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x),
+                                                                 CTRL, 0xF, 0xF, false));
+}
+
+// DPP controls (GFX9 encoding).
+constexpr int DPP_QUAD_XOR1 = 0xB1;   // quad_perm [1,0,3,2]
+constexpr int DPP_QUAD_XOR2 = 0x4E;   // quad_perm [2,3,0,1]
+constexpr int DPP_ROW_MIRROR = 0x140;
+constexpr int DPP_ROW_HALF_MIRROR = 0x141;
+
+// Reduce within each row of 16 lanes; every lane of the row ends with the same value
+// (max and + are commutative, so both partners of each step compute identical bits).
+__device__ __forceinline__ float row_max16(float x) {
+    x = fmaxf(x, dpp<DPP_QUAD_XOR1>(x));
+    x = fmaxf(x, dpp<DPP_QUAD_XOR2>(x));
+    x = fmaxf(x, dpp<DPP_ROW_HALF_MIRROR>(x));
+    x = fmaxf(x, dpp<DPP_ROW_MIRROR>(x));
+    return x;
+}
+
+__device__ __forceinline__ float row_sum16(float x) {
+    x = x + dpp<DPP_QUAD_XOR1>(x);
+    x = x + dpp<DPP_QUAD_XOR2>(x);
+    x = x + dpp<DPP_ROW_HALF_MIRROR>(x);
+    x = x + dpp<DPP_ROW_MIRROR>(x);
+    return x;
+}
+
+__device__ __forceinline__ float lane_read(float x, int lane) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), lane));
+}
+
+// Wave-uniform max / sum over all 64 lanes (fixed order, so bit-reproducible).
+__device__ __forceinline__ float wave_max(float x) {
+    x = row_max16(x);
+    return fmaxf(fmaxf(lane_read(x, 0), lane_read(x, 16)), fmaxf(lane_read(x, 32), lane_read(x, 48)));
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+    x = row_sum16(x);
+    return (lane_read(x, 0) + lane_read(x, 16)) + (lane_read(x, 32) + lane_read(x, 48));
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+}  // namespace kvp

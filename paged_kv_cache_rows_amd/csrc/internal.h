@@ -1,0 +1,59 @@
+// Internal declarations shared by the host API and the kernel translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace kvp {
+
+// Arguments of the row-write kernel.
+struct RowsArgs {
+    uint16_t *k_pages;
+    uint16_t *v_pages;
+    const uint16_t *k_new;
+    const uint16_t *v_new;
+    const int32_t *table;
+    const int32_t *seq_len;
+    int num_pages, P, Hkv, D;
+    int S, R, stride, ring_pages;
+};
+
+// Arguments of the split-context part kernels (VALU and MFMA).  Each workgroup handles one
+// (stream, KV head, key chunk[, query tile]) and writes an unnormalised partial result:
+// acc[D] plus (m, l) per query vector, m in log2 units.
+struct PartArgs {
+    const uint16_t *k_pages;
+    const uint16_t *v_pages;
+    const int32_t *table;
+    const int32_t *seq_len;
+    const uint16_t *q;
+    float *ws_acc;   // [S][R][Hq][n_splits][D]
+    float *ws_ml;    // [S][R][Hq][n_splits][2]
+    int num_pages, P, Hkv, stride, ring_pages;
+    int R, Hq, window, n_splits;
+    float scale_log2;  // scale * log2(e)
+};
+
+struct MergeArgs {
+    const float *ws_acc;
+    const float *ws_ml;
+    const int32_t *seq_len;
+    uint16_t *out;   // [S][R][Hq][D]
+    int S, R, Hq, D, window, n_splits, chunk;
+};
+
+// Keys per split (workgroup) of each path; split boundaries are multiples of this in absolute
+// positions, so they depend on (L, R, W, D) only and never on physical page ids.
+int valu_chunk(int D);
+int mfma_chunk(int D);
+bool valu_supported(int D, int G, int NQ);
+bool mfma_supported(int D, int G, int R);
+int mfma_query_tiles(int D, int G, int R);  // query tiles per (stream, KV head)
+
+hipError_t launch_rows_put(const RowsArgs &a, hipStream_t st);
+hipError_t launch_part_valu(int D, int G, int NQ, const PartArgs &a, int S, hipStream_t st);
+hipError_t launch_part_mfma(int D, int G, const PartArgs &a, int S, hipStream_t st);
+hipError_t launch_merge(const MergeArgs &a, hipStream_t st);
+
+}  // namespace kvp

@@ -1,0 +1,218 @@
+"""Host-side tests of the C-ABI library (no GPU needed; no kernel is launched).
+
+* The built library exports exactly the entry points include/kvpaged.h declares (an ABI
+  tripwire: a new or missing export fails here).
+* Bad arguments are refused with the documented status before any launch, and leave no state
+  change.
+* Leases and releases hand out exactly the ids the oracle's lease model predicts.
+"""
+import ctypes
+import os
+import random
+import re
+import subprocess
+
+import pytest
+
+import torch
+
+import oracle
+from paged_kv_cache_rows_amd import binding
+
+# The refusal tests pass made-up device addresses that the checks must reject before any
+# launch.  They are host-logic tests for a CPU-only machine: on a GPU host a check that wrongly
+# let a case through would launch on those addresses, so they are skipped there.
+host_only = pytest.mark.skipif(torch.cuda.is_available(), reason="fake device pointers; CPU-only host")
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kvpaged.h")
+CSRC = os.path.join(ROOT, "paged_kv_cache_rows_amd", "csrc")
+
+
+def _newest_source_mtime():
+    paths = [HEADER] + [os.path.join(CSRC, f) for f in os.listdir(CSRC)]
+    return max(os.path.getmtime(p) for p in paths)
+
+
+@pytest.fixture(scope="session")
+def lib():
+    if not os.path.exists(binding.LIB_PATH) or os.path.getmtime(binding.LIB_PATH) < _newest_source_mtime():
+        from paged_kv_cache_rows_amd import build
+        build.build()
+    return binding.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*([a-z_0-9]+)\s*\(", text, flags=re.M))
+
+
+def test_header_declares_the_six_named_entry_points():
+    names = declared_functions()
+    for n in ("kv_pool_create", "kv_page_lease", "kv_rows_put", "paged_attn_decode",
+              "paged_attn_verify", "paged_attn_prefill"):
+        assert n in names
+    assert names == set(binding.EXPORTS)
+
+
+def test_library_exports_exactly_the_declared_symbols(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", binding.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    exported = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
+    ours = {s for s in exported if s.startswith(("kv_", "paged_attn_"))}
+    assert ours == declared_functions()
+    for name in declared_functions():
+        assert hasattr(lib, name)
+    assert binding.abi_version() == 1
+
+
+def _desc(num_pages=8, P=64, Hkv=1, D=128, streams=2, order=None):
+    # Host-only calls never dereference the page pointers; any 16-byte aligned value will do.
+    fo = None
+    keep = None
+    if order is not None:
+        keep = (ctypes.c_int32 * len(order))(*order)
+        fo = ctypes.cast(keep, ctypes.POINTER(ctypes.c_int32))
+    d = binding.PoolDesc(num_pages, P, Hkv, D, streams, 0x10000, 0x20000, fo)
+    return d, keep
+
+
+def _create(lib, **kw):
+    d, keep = _desc(**kw)
+    h = ctypes.c_void_p()
+    st = lib.kv_pool_create(ctypes.byref(d), ctypes.byref(h))
+    return st, h, keep
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(num_pages=0), binding.KV_E_ARG),
+    (dict(P=0), binding.KV_E_ARG),
+    (dict(D=12), binding.KV_E_ARG),
+    (dict(streams=0), binding.KV_E_ARG),
+    (dict(order=[0, 1, 2, 3, 4, 5, 6, 6]), binding.KV_E_ARG),
+    (dict(order=[0, 1, 2, 3, 4, 5, 6, 8]), binding.KV_E_ARG),
+])
+def test_pool_create_refuses_bad_geometry(lib, kw, status):
+    st, h, _ = _create(lib, **kw)
+    assert st == status and not h.value
+    assert lib.kv_last_error()
+
+
+def test_lease_is_all_or_nothing(lib):
+    st, h, _ = _create(lib, num_pages=8)
+    assert st == 0
+    ids = (ctypes.c_int32 * 16)()
+    assert lib.kv_page_lease(h, 0, 5, ids) == 0
+    assert list(ids[:5]) == [0, 1, 2, 3, 4]
+    n = ctypes.c_int32()
+    assert lib.kv_page_lease(h, 1, 4, ids) == binding.KV_E_NO_PAGES
+    lib.kv_pool_free_count(h, ctypes.byref(n))
+    assert n.value == 3
+    assert lib.kv_page_lease(h, 2, 1, ids) == binding.KV_E_ARG        # stream out of range
+    assert lib.kv_page_lease(h, 0, -1, ids) == binding.KV_E_ARG
+    assert lib.kv_page_release(h, 0) == 0
+    lib.kv_pool_free_count(h, ctypes.byref(n))
+    assert n.value == 8
+    lib.kv_pool_destroy(h)
+
+
+@pytest.mark.parametrize("seed", range(5))
+def test_leases_match_the_oracle_model(lib, seed):
+    rng = random.Random(seed)
+    N, S = 60, 6
+    order = list(range(N))
+    rng.shuffle(order)
+    st, h, keep = _create(lib, num_pages=N, streams=S, order=order)
+    assert st == 0
+    model = oracle.LeaseModel(N, S, order)
+    buf = (ctypes.c_int32 * N)()
+    for _ in range(300):
+        s = rng.randrange(S)
+        if rng.random() < 0.65:
+            n = rng.randrange(0, 15)
+            st = lib.kv_page_lease(h, s, n, buf)
+            try:
+                want = model.lease(s, n)
+                assert st == 0 and list(buf[:n]) == want
+            except oracle.NoPages:
+                assert st == binding.KV_E_NO_PAGES
+        else:
+            assert lib.kv_page_release(h, s) == 0
+            model.release(s)
+        cnt = ctypes.c_int32()
+        lib.kv_pool_free_count(h, ctypes.byref(cnt))
+        assert cnt.value == model.free_count
+        got_n = ctypes.c_int32()
+        assert lib.kv_stream_pages(h, s, buf, N, ctypes.byref(got_n)) == 0
+        assert list(buf[:got_n.value]) == model.leased[s]
+    lib.kv_pool_destroy(h)
+
+
+def _layout(S=1, R=1, stride=8, max_len=300, ring=0):
+    # Device pointers are never dereferenced by the refusals tested here.
+    return binding.Layout(S, R, 0x30000, stride, 0x40000, max_len, ring)
+
+
+def _args(Hq=16, window=0, ws=0x50000, nbytes=1 << 30, scale=0.0):
+    return binding.AttnArgs(0x60000, 0x70000, Hq, scale, window, ws, nbytes)
+
+
+@pytest.mark.parametrize("entry,lay,args,status", [
+    ("paged_attn_decode", _layout(R=2), _args(), binding.KV_E_ARG),            # decode needs R == 1
+    ("paged_attn_verify", _layout(R=9), _args(), binding.KV_E_ARG),            # verify is 1..8 rows
+    ("paged_attn_prefill", _layout(R=0), _args(), binding.KV_E_ARG),
+    ("paged_attn_decode", _layout(stride=4), _args(), binding.KV_E_ARG),       # table too short for 300/64
+    ("paged_attn_decode", _layout(), _args(Hq=6), binding.KV_E_ARG),           # Hq not a multiple of Hkv = 4
+    ("paged_attn_decode", _layout(), _args(Hq=12), binding.KV_E_SHAPE),        # group 3: no kernel
+    ("paged_attn_decode", _layout(), _args(nbytes=16), binding.KV_E_WORKSPACE),
+    ("paged_attn_decode", _layout(), _args(ws=0x50010), binding.KV_E_ARG),     # workspace misaligned
+    ("paged_attn_decode", _layout(), _args(window=-1), binding.KV_E_ARG),
+    ("paged_attn_decode", _layout(), _args(scale=-1.0), binding.KV_E_ARG),
+    ("paged_attn_decode", _layout(ring=2), _args(), binding.KV_E_ARG),         # ring without a window
+    ("paged_attn_decode", _layout(ring=2), _args(window=200), binding.KV_E_ARG),  # ring 128 < window
+    ("paged_attn_verify", _layout(max_len=3, R=4), _args(), binding.KV_E_ARG),   # R > max_seq_len
+])
+@host_only
+def test_attention_refuses_before_launch(lib, entry, lay, args, status):
+    d = binding.PoolDesc(8, 64, 4, 128, 2, 0x10000, 0x20000, None)
+    h = ctypes.c_void_p()
+    assert lib.kv_pool_create(ctypes.byref(d), ctypes.byref(h)) == 0
+    st = getattr(lib, entry)(h, ctypes.byref(lay), ctypes.byref(args), None)
+    assert st == status, lib.kv_last_error()
+    assert lib.kv_last_error()
+    lib.kv_pool_destroy(h)
+
+
+def test_head_dim_without_kernel_is_a_shape_error(lib):
+    d = binding.PoolDesc(8, 64, 1, 64, 2, 0x10000, 0x20000, None)
+    h = ctypes.c_void_p()
+    assert lib.kv_pool_create(ctypes.byref(d), ctypes.byref(h)) == 0
+    n = ctypes.c_size_t()
+    st = lib.paged_attn_workspace_size(h, ctypes.byref(_layout()), ctypes.byref(_args(Hq=4)), ctypes.byref(n))
+    assert st == binding.KV_E_SHAPE
+    lib.kv_pool_destroy(h)
+
+
+def test_workspace_size_depends_on_shape_only(lib):
+    d = binding.PoolDesc(100, 512, 8, 128, 12, 0x10000, 0x20000, None)
+    h = ctypes.c_void_p()
+    assert lib.kv_pool_create(ctypes.byref(d), ctypes.byref(h)) == 0
+    n = ctypes.c_size_t()
+    lay = binding.Layout(12, 1, 0x30000, 80, 0x40000, 40960, 0)
+    assert lib.paged_attn_workspace_size(h, ctypes.byref(lay), ctypes.byref(_args(Hq=64)), ctypes.byref(n)) == 0
+    # 12 streams x 64 heads x 40 splits of 1024 keys x (128 + 2) floats
+    assert n.value == 12 * 64 * 40 * 130 * 4
+    lib.kv_pool_destroy(h)
+
+
+@host_only
+def test_rows_put_refuses_bad_layouts(lib):
+    d = binding.PoolDesc(8, 64, 1, 128, 2, 0x10000, 0x20000, None)
+    h = ctypes.c_void_p()
+    assert lib.kv_pool_create(ctypes.byref(d), ctypes.byref(h)) == 0
+    assert lib.kv_rows_put(h, ctypes.byref(_layout(R=0)), 0x1000, 0x2000, None) == binding.KV_E_ARG
+    assert lib.kv_rows_put(h, ctypes.byref(_layout()), None, 0x2000, None) == binding.KV_E_ARG
+    assert lib.kv_rows_put(h, ctypes.byref(_layout(ring=1, R=65, max_len=300)), 0x1000, 0x2000, None) == binding.KV_E_ARG
+    assert lib.kv_rows_put(None, ctypes.byref(_layout()), 0x1000, 0x2000, None) == binding.KV_E_ARG
+    lib.kv_pool_destroy(h)
