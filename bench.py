@@ -1,0 +1,257 @@
+"""Benchmark of the paged decode hot path on one MI355X.
+
+A step is one layer's decode for 12 streams: kv_rows_put of each stream's new K/V row, then
+paged_attn_decode (split-context part kernel + merge) over contexts uniform in
+[32768, 40960] with 8 KV / 64 query heads, head_dim 128, bf16, pages of 512 shuffled over the
+pool.  Inputs are resident in HBM before the timed region starts.
+
+Prints one JSON line: `value` is K/V bytes read per step over the measured step time (GB/s,
+whole job), `roofline` compares the part kernel's average duration (HIP events recorded on
+the kernel's stream around every launch in the timed region) with the 8 TB/s HBM peak, and
+`cpu_baseline` times the float64 oracle on a bounded sample of the same workload.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline] [--quick]
+"""
+import argparse
+import hashlib
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "paged-attn decode µs/layer + K/V HBM GB/s (% peak), 12 streams x 40k ctx"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "part_valu_d128_g8_batched_decode_traffic.json")
+KERNEL_SOURCE = os.path.join(ROOT, "paged_kv_cache_rows_amd", "csrc", "kernels_valu.hip")
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--quick", action="store_true", help="skip the side measurements")
+    ap.add_argument("--fixed-length", type=int, default=None, help="all 12 streams at this length")
+    return ap.parse_args()
+
+
+def source_digest() -> str:
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they were taken on the
+    current kernel source; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_sha256") != source_digest():
+        return None
+    return t.get("bytes_per_launch")
+
+
+class DecodeSetup:
+    def __init__(self, w, order_seed, torch, binding, staging, workloads, identity=False):
+        self.w = w
+        self.torch = torch
+        order = (workloads.identity_order(w.pool_pages) if identity
+                 else workloads.free_order(w.pool_pages, order_seed))
+        self.c = staging.make_cache(w, device="cuda", order=order)
+        self.ks, self.vs = workloads.kv_history(w, device="cuda")
+        staging.write_history(self.c, self.ks, self.vs)
+        self.q = workloads.queries(w, device="cuda")
+        # the step's new rows are the last rows of each stream's history (rewritten in place)
+        self.k_new = torch.stack([k[-1:] for k in self.ks]).contiguous()
+        self.v_new = torch.stack([v[-1:] for v in self.vs]).contiguous()
+        self.out = torch.empty_like(self.q)
+        nbytes = binding.workspace_size(self.c.pool, self.c.table, self.c.seq_len, 1, w.q_heads,
+                                        self.c.max_seq_len)
+        self.ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+        self.binding = binding
+        self.kv_bytes = sum(self.c.lengths) * w.kv_bytes_per_token
+
+    def step(self):
+        b, c = self.binding, self.c
+        b.rows_put(c.pool, c.table, c.seq_len, self.k_new, self.v_new, c.max_seq_len)
+        b.decode(c.pool, self.q, c.table, c.seq_len, c.max_seq_len, out=self.out, workspace=self.ws)
+
+    def attention_only(self):
+        c = self.c
+        self.binding.decode(c.pool, self.q, c.table, c.seq_len, c.max_seq_len, out=self.out, workspace=self.ws)
+
+
+def timed_steps(setup, steps, warmup, torch, binding):
+    """Wall time per step over `steps` back-to-back steps, and the part kernel's average
+    duration from HIP events recorded around each of its launches."""
+    for _ in range(warmup):
+        setup.step()
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    stops = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    for e in starts + stops:
+        e.record()                      # materialise the underlying hipEvent_t
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        binding.set_part_events(starts[i].cuda_event, stops[i].cuda_event)
+        setup.step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    binding.set_part_events(None, None)
+    part_ms = [starts[i].elapsed_time(stops[i]) for i in range(steps)]
+    return (t1 - t0) * 1e3 / steps, sum(part_ms) / steps, min(part_ms), max(part_ms)
+
+
+def cold_calls(setup, iters, torch):
+    """Event-timed attention calls each preceded by a 1 GiB write that evicts L2 and MALL."""
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    ms = []
+    for _ in range(iters):
+        flush.fill_(1)
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        setup.attention_only()
+        b.record()
+        torch.cuda.synchronize()
+        ms.append(a.elapsed_time(b))
+    ms.sort()
+    return ms[len(ms) // 2]
+
+
+def cpu_baseline(setup, oracle, workloads, budget_s=20.0):
+    """The oracle, as it stands, on streams of the same workload until about budget_s of CPU
+    work: gather through the table walk, widen to float64, attend.  Returns a dict in GB/s of
+    K/V processed."""
+    import numpy as np
+    c, w = setup.c, setup.w
+    kb = workloads.bf16_bits(c.pool.k_pages)
+    vb = workloads.bf16_bits(c.pool.v_pages)
+    qb = workloads.bf16_bits(setup.q)
+    done, nbytes, secs = [], 0, 0.0
+    for s in range(w.streams):
+        L = c.lengths[s]
+        t0 = time.perf_counter()
+        kl = oracle.bf16_bits_to_f64(oracle.gather_linear(kb, c.table_host[s], L, w.page_size))
+        vl = oracle.bf16_bits_to_f64(oracle.gather_linear(vb, c.table_host[s], L, w.page_size))
+        out = oracle.attend_stream(oracle.bf16_bits_to_f64(qb[s]), kl, vl, 1, 0, length=L)
+        secs += time.perf_counter() - t0
+        assert np.isfinite(out).all()
+        done.append(s)
+        nbytes += L * w.kv_bytes_per_token
+        if secs >= budget_s:
+            break
+    cores = len(os.sched_getaffinity(0))
+    return {"value": round(nbytes / secs / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "sample": f"float64 oracle (table walk + widen + attend) on streams {done[0]}..{done[-1]} "
+                      f"of 12 ({nbytes / 1e9:.3f} GB of K/V) in {secs:.2f} s; numpy/BLAS may use all "
+                      f"{cores} threads; host {platform.processor() or platform.machine()}"}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (the paged decode "
+              "runs per GPU on its own streams); run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import oracle
+    from paged_kv_cache_rows_amd import binding, staging, workloads
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    binding.load()
+    torch.cuda.set_device(0)
+
+    w = workloads.batched_decode(fixed_length=args.fixed_length)
+    log(f"[bench] building {w.name}: lengths {w.lengths}, pool {w.pool_pages} pages")
+    setup = DecodeSetup(w, 3002, torch, binding, staging, workloads)
+    torch.cuda.synchronize()
+    log("[bench] timing steps")
+    ms_step, part_ms, part_min, part_max = timed_steps(setup, args.steps, args.warmup, torch, binding)
+    value = setup.kv_bytes / (ms_step * 1e-3) / 1e9
+    achieved = setup.kv_bytes / (part_ms * 1e-3) / 1e9
+    traffic = measured_traffic()
+    log(f"[bench] {ms_step * 1e3:.1f} us/step, part kernel {part_ms * 1e3:.1f} us, {achieved:.0f} GB/s")
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{w.name}: 12 streams, contexts U[32768, 40960] (seed 2002), 8 KV / 64 query "
+                        f"heads, head_dim 128, bf16 K/V, pages of 512 shuffled over a pool with 10% NaN "
+                        f"spares; step = kv_rows_put (1 row/stream) + paged_attn_decode"
+            if args.fixed_length is None else
+            f"{w.name}: 12 streams x {args.fixed_length}, otherwise as the batched decode",
+            "streams": w.streams, "kv_heads": w.kv_heads, "q_heads": w.q_heads, "head_dim": w.head_dim,
+            "page_size": w.page_size, "rows": 1, "lengths": w.lengths,
+            "kv_bytes_per_step": setup.kv_bytes,
+        },
+        "us_per_layer": round(ms_step * 1e3, 2),
+        "roofline": {
+            "bound": "hbm", "kernel": "part_valu_kernel<128,8,8>",
+            "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "part_us_mean": round(part_ms * 1e3, 2), "part_us_min": round(part_min * 1e3, 2),
+            "part_us_max": round(part_max * 1e3, 2),
+        },
+    }
+
+    if not args.quick:
+        log("[bench] cold-cache calls (1 GiB flush before each)")
+        result["cold_attention_us"] = round(cold_calls(setup, 20, torch) * 1e3, 2)
+        log("[bench] identity-table (linear) arm")
+        lin = DecodeSetup(w, 0, torch, binding, staging, workloads, identity=True)
+        lms, lpart, _, _ = timed_steps(lin, max(20, args.steps // 4), 5, torch, binding)
+        result["identity_table"] = {"us_per_layer": round(lms * 1e3, 2), "part_us_mean": round(lpart * 1e3, 2),
+                                    "paged_over_identity": round(part_ms / lpart, 4)}
+        same = torch.equal(lin.out.view(torch.int16), setup.out.view(torch.int16))
+        result["identity_table"]["bytes_equal"] = bool(same)
+        del lin
+        torch.cuda.empty_cache()
+        if args.fixed_length is None:
+            log("[bench] fixed 12 x 40960 variant")
+            wf = workloads.batched_decode(fixed_length=40960)
+            fx = DecodeSetup(wf, 3002, torch, binding, staging, workloads)
+            fms, fpart, _, _ = timed_steps(fx, max(20, args.steps // 4), 5, torch, binding)
+            result["fixed_12x40960"] = {"us_per_layer": round(fms * 1e3, 2), "part_us_mean": round(fpart * 1e3, 2),
+                                        "kv_GBps": round(fx.kv_bytes / (fms * 1e-3) / 1e9, 1),
+                                        "part_kv_GBps": round(fx.kv_bytes / (fpart * 1e-3) / 1e9, 1)}
+            del fx
+            torch.cuda.empty_cache()
+
+    if not args.no_cpu_baseline:
+        log("[bench] cpu baseline (oracle)")
+        result["cpu_baseline"] = cpu_baseline(setup, oracle, workloads)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -2,13 +2,13 @@
  * kvpaged.h -- C ABI of a paged KV cache and attention over it, for MI355X (gfx950).
  *
  * The operation (TensorFold PR #1620, paged K/V for Kolibri-1's full layers, opening
- * description): the full layers keep K and V in fixed-size pages of one shared pool
- * ("pages of 512 positions"; the kernel-contract bullet also runs pages of 37 and 64), every
- * stream leases pages as it grows, new rows are copied into their page slots ("Writes"
- * bullet), and attention reads keys through a per-stream page table given in the call's
- * stream order ("Reads" bullet); sliding layers keep rings.  Decode and drafted verify read
- * through the table, with verify windows of 1..8 causal rows (TensorFold PR #2730: the
- * pending token plus up to seven drafts), and prompts have their own paged kernels.
+ * description): the full layers keep K and V in fixed-size pages of one shared pool (512
+ * positions per page; the kernel-contract bullet also runs pages of 37 and 64), every stream
+ * leases pages as it grows, new rows are copied into their page slots (the Writes bullet), and
+ * attention reads keys through a per-stream page table passed in the call's stream order (the
+ * Reads bullet); sliding layers keep ring buffers instead.  Decode and drafted verify read
+ * through the table, with verify windows of 1..8 causal rows (TensorFold PR #2730, What this
+ * changes: the pending token and up to seven drafts), and prompts have their own paged kernels.
  *
  * Conventions shared by every call:
  *   - Every call returns kv_status.  Nothing aborts, throws or synchronises the device.  On a
@@ -96,8 +96,9 @@ typedef struct kv_attn_args {
     size_t workspace_bytes;
 } kv_attn_args;
 
-/* Create a pool over caller-owned pages (TensorFold PR #1620, opening description: "Arena,
- * plan and leasing" -- the arena is the caller's pair of page arrays, leasing is below).
+/* Create a pool over caller-owned pages (TensorFold PR #1620, opening description: the pool
+ * is an arena planned for the streams and leased out; here the arena is the caller's pair of
+ * page arrays and the leasing is below).
  * Errors: KV_E_ARG for a null desc/out/page pointer, a non-positive size, D not a multiple of
  * 8, or a free_order that is not a permutation of [0, num_pages). */
 kv_status kv_pool_create(const kv_pool_desc *desc, kv_pool **out);
@@ -105,15 +106,15 @@ kv_status kv_pool_create(const kv_pool_desc *desc, kv_pool **out);
 /* Destroy the host metadata (never the caller's pages).  NULL is accepted. */
 kv_status kv_pool_destroy(kv_pool *pool);
 
-/* Lease n pages to a stream as it grows (TensorFold PR #1620, opening description: "every
- * stream leasing as it grows").  Pages come off the front of the free queue in queue order,
+/* Lease n pages to a stream as it grows (TensorFold PR #1620, opening description: streams
+ * take pages from the shared pool as their caches grow).  Pages come off the front of the free queue in queue order,
  * are appended to the stream's lease list and are written to page_ids_out (host [n]).
  * All or nothing: with fewer than n free pages it returns KV_E_NO_PAGES and changes nothing.
  * KV_E_ARG for a bad stream id, n < 0, or a null output with n > 0.  Thread-safe per pool. */
 kv_status kv_page_lease(kv_pool *pool, int32_t stream, int32_t n, int32_t *page_ids_out);
 
 /* Return all of a stream's pages to the back of the free queue, in the order they were leased
- * (released pages are reused by later leases: the model test's "reused pages").  KV_E_ARG for
+ * (released pages are handed out again by later leases, which the PR's model test covers).  KV_E_ARG for
  * a bad stream id.  The pages' contents are left as they are. */
 kv_status kv_page_release(kv_pool *pool, int32_t stream);
 
@@ -126,7 +127,7 @@ kv_status kv_stream_pages(const kv_pool *pool, int32_t stream, int32_t *ids_out,
                           int32_t *n_out);
 
 /* Write each stream's R new K and V rows into their page slots (TensorFold PR #1620, opening
- * description, "Writes" bullet: the rows kernel's new K/V rows are copied into the pages).
+ * description, Writes bullet: the K/V rows a layer produces are copied into the pages).
  * k_new, v_new: device bf16 [S][R][Hkv][D].  Row r of stream s goes to position
  * seq_len[s] - R + r, i.e. page table[s][pos / P] (or ring slot (pos / P) % ring_pages) at
  * slot pos % P, for every KV head.  Rows at negative positions are skipped.  Every other byte
@@ -140,7 +141,7 @@ kv_status paged_attn_workspace_size(const kv_pool *pool, const kv_layout *lay,
                                     const kv_attn_args *a, size_t *bytes);
 
 /* Paged GQA attention for one decode row per stream (R == 1) (TensorFold PR #1620, opening
- * description, "Reads" bullet: decode reads keys from a page table).  For each stream s and
+ * description, Reads bullet: decode reads its keys through the page table).  For each stream s and
  * query head h: out = softmax(scale * q K^T) V over the keys the row sees (all positions
  * 0..L-1, or the newest `window`), K and V read through the stream's page table.  Computed
  * with fp32 accumulation; the output is rounded to bf16 (nearest even).  Results depend only
@@ -151,18 +152,24 @@ kv_status paged_attn_decode(const kv_pool *pool, const kv_layout *lay, const kv_
                             void *hip_stream);
 
 /* The same for a speculative verify window of 1 <= R <= 8 causal rows per stream (TensorFold
- * PR #2730: the pending token plus up to seven drafts; "the window kernels already take any row
- * count").  Row r sits at position L-R+r and sees keys up to and including itself.
+ * PR #2730, What this changes: the pending token plus up to seven drafts, and the window
+ * kernels accept any row count).  Row r sits at position L-R+r and sees keys up to and including itself.
  * Errors as for decode, with KV_E_ARG for R outside 1..8. */
 kv_status paged_attn_verify(const kv_pool *pool, const kv_layout *lay, const kv_attn_args *a,
                             void *hip_stream);
 
 /* The same for a prompt chunk of any R >= 1 causal rows per stream (TensorFold PR #1620,
- * opening description, "Reads" bullet: prompts go through paged prompt kernels).  A prompt is
+ * opening description, Reads bullet: prompts have paged prompt kernels of their own).  A prompt is
  * processed chunk by chunk: kv_rows_put the chunk's rows, then this call with R = chunk rows.
  * Errors as for decode, with KV_E_ARG for R < 1. */
 kv_status paged_attn_prefill(const kv_pool *pool, const kv_layout *lay, const kv_attn_args *a,
                              void *hip_stream);
+
+/* Measurement hook: when both are non-NULL, every later attention call made by this thread
+ * records hipEvent_t `start` on its stream just before its part kernel (the one that streams K
+ * and V) and `stop` just after it, so the caller can time that kernel alone with
+ * hipEventElapsedTime.  NULL, NULL turns it off.  The events are the caller's. */
+kv_status kv_set_part_events(void *start_event, void *stop_event);
 
 /* Text of the calling thread's last non-OK status ("" if none). */
 const char *kv_last_error(void);

@@ -6,10 +6,10 @@ never does, and this package never imports the product path.
 
 What it computes (TensorFold PR #1620, paged K/V for Kolibri-1's full layers):
   * `pages.gather_linear`   walks a stream's page table to rebuild its linear cache
-                            (opening description, "Reads" bullet: keys are read through a
+                            (opening description, Reads bullet: keys are read through a
                             per-stream page table).
   * `pages.rows_put`        scatters a call's new K/V rows into their page slots
-                            (opening description, "Writes" bullet).
+                            (opening description, Writes bullet).
   * `attention.attend`      softmax(q k^T / sqrt(d)) v over the linear cache, with GQA, causal
                             verify rows and an optional sliding window, all in float64 (the
                             author's kernel-timing reply: the paged kernels read the same

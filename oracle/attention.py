@@ -1,13 +1,13 @@
 """Float64 attention over a linear cache (test infrastructure only).
 
-Definition followed (TensorFold PR #1620; the pages print no formula, so the plain reading of
-"attention reads keys from a page table" plus "the addresses are the same, so the bits are the
-same" from the author's kernel-timing reply is taken: paged attention equals attention over the
-stream's linear cache):
+Definition followed (TensorFold PR #1620; the pages print no formula.  The plainest reading is
+taken: the Reads bullet says attention reads its keys through a page table, and the author's
+kernel-timing reply says the paged kernels read the very same keys as the linear ones and so
+produce identical bits; hence paged attention equals attention over the stream's linear cache):
 
   For stream s with cache length L (after this call's R rows were written), row r of the call
-  sits at position p_r = L - R + r (rows are written before they are read: the "Writes" bullet
-  precedes the "Reads" bullet).  Query head h reads KV head h // G (heads grouped contiguously;
+  sits at position p_r = L - R + r (rows are written before they are read: the Writes bullet
+  comes before the Reads bullet).  Query head h reads KV head h // G (heads grouped contiguously;
   the pages give only head counts such as 48/4 and 16/1).  Row r sees keys
   j in [0, p_r] for full layers, or j in [p_r - W + 1, p_r] for a sliding layer of window W
   (W keys including itself; the pages say only that sliding layers keep rings).

@@ -1,8 +1,8 @@
 """Plain Python model of the shared page pool (test infrastructure only).
 
 TensorFold PR #1620, opening description: the full layers' caches live in pages of one core
-pool and every stream leases pages as it grows; the "Kept states" bullet and the model test
-("reused pages") say released pages are handed out again.  The pages give no hand-out order,
+pool and every stream leases pages as it grows; the Kept states bullet and the model test
+say released pages are handed out again.  The pages give no hand-out order,
 so this library fixes one and the model states it:
 
   * The free list is a FIFO queue, initialised with `free_order` (default 0, 1, ..., N-1).

@@ -4,8 +4,8 @@ Pool layout (this library's choice; the pages do not fix one): K and V pages are
 [num_pages][Hkv][P][D] of bf16, so one KV head's rows inside a page are contiguous.
 
 TensorFold PR #1620, opening description: pages of 512 positions leased from the core pool,
-"Writes" (new rows copied into their page slots) and "Reads" (keys read through a per-stream
-page table in the call's stream order); sliding layers keep rings.  Positions map to slots as:
+the Writes bullet (new rows copied into their page slots) and the Reads bullet (keys read through
+a per-stream page table in the call's stream order); sliding layers keep rings.  Positions map to slots as:
     full layer:  page = table[j // P],                  slot = j % P
     ring layer:  page = table[(j // P) % ring_pages],   slot = j % P
 so a ring of n pages holds the newest n*P positions.

@@ -26,8 +26,8 @@ STATUS_NAMES = {0: "KV_OK", -1: "KV_E_ARG", -2: "KV_E_SHAPE", -3: "KV_E_NO_PAGES
 # The entry points include/kvpaged.h declares (checked against the built library's exports).
 EXPORTS = ("kv_pool_create", "kv_pool_destroy", "kv_page_lease", "kv_page_release",
            "kv_pool_free_count", "kv_stream_pages", "kv_rows_put", "paged_attn_workspace_size",
-           "paged_attn_decode", "paged_attn_verify", "paged_attn_prefill", "kv_last_error",
-           "kv_abi_version")
+           "paged_attn_decode", "paged_attn_verify", "paged_attn_prefill", "kv_set_part_events",
+           "kv_last_error", "kv_abi_version")
 
 
 class KvError(RuntimeError):
@@ -77,6 +77,7 @@ def load(path: str = LIB_PATH):
         "paged_attn_decode": [c_void_p, POINTER(Layout), POINTER(AttnArgs), c_void_p],
         "paged_attn_verify": [c_void_p, POINTER(Layout), POINTER(AttnArgs), c_void_p],
         "paged_attn_prefill": [c_void_p, POINTER(Layout), POINTER(AttnArgs), c_void_p],
+        "kv_set_part_events": [c_void_p, c_void_p],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -245,6 +246,12 @@ def verify(pool, q, table, seq_len, max_seq_len, **kw):
 def prefill(pool, q, table, seq_len, max_seq_len, **kw):
     """paged_attn_prefill: a prompt chunk of any number of causal rows per stream."""
     return _attend("paged_attn_prefill", pool, q, table, seq_len, max_seq_len, **kw)
+
+
+def set_part_events(start: int | None, stop: int | None):
+    """Record the given hipEvent_t handles around the part kernel of later attention calls
+    (None, None turns it off)."""
+    _check(load().kv_set_part_events(start, stop))
 
 
 def abi_version() -> int:

@@ -27,6 +27,8 @@ struct kv_pool {
 namespace {
 
 thread_local std::string g_last_error;
+thread_local hipEvent_t g_part_start = nullptr;
+thread_local hipEvent_t g_part_stop = nullptr;
 
 kv_status fail(kv_status st, const char *fmt, ...) {
     char buf[512];
@@ -190,9 +192,13 @@ kv_status run_attention(const kv_pool *pool, const kv_layout *lay, const kv_attn
     const float scale = a->scale > 0.f ? a->scale : 1.0f / std::sqrt((float)p.D);
     pa.scale_log2 = scale * 1.4426950408889634f;
 
+    if (g_part_start && hipEventRecord(g_part_start, hs) != hipSuccess)
+        return fail(KV_E_DEVICE, "%s: recording the start event failed", who);
     hipError_t e = p.mfma ? kvp::launch_part_mfma(p.D, p.G, pa, p.S, hs)
                           : kvp::launch_part_valu(p.D, p.G, p.R * p.G, pa, p.S, hs);
     if (e != hipSuccess) return fail(KV_E_DEVICE, "%s: part kernel launch failed: %s", who, hipGetErrorString(e));
+    if (g_part_stop && hipEventRecord(g_part_stop, hs) != hipSuccess)
+        return fail(KV_E_DEVICE, "%s: recording the stop event failed", who);
 
     kvp::MergeArgs ma;
     ma.ws_acc = pa.ws_acc;
@@ -362,6 +368,14 @@ kv_status paged_attn_verify(const kv_pool *pool, const kv_layout *lay, const kv_
 kv_status paged_attn_prefill(const kv_pool *pool, const kv_layout *lay, const kv_attn_args *a, void *hip_stream) {
     if (lay && lay->rows < 1) return fail(KV_E_ARG, "paged_attn_prefill: rows %d < 1", lay->rows);
     return run_attention(pool, lay, a, hip_stream, "paged_attn_prefill");
+}
+
+kv_status kv_set_part_events(void *start_event, void *stop_event) {
+    if ((start_event == nullptr) != (stop_event == nullptr))
+        return fail(KV_E_ARG, "kv_set_part_events: give both events or neither");
+    g_part_start = static_cast<hipEvent_t>(start_event);
+    g_part_stop = static_cast<hipEvent_t>(stop_event);
+    return ok();
 }
 
 const char *kv_last_error(void) { return g_last_error.c_str(); }

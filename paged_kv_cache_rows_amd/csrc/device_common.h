@@ -8,6 +8,7 @@
 namespace kvp {
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 // c + a.lo * b.lo + a.hi * b.hi, bf16 inputs, fp32 accumulate (v_dot2c_f32_bf16).
 __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
@@ -74,5 +75,13 @@ __device__ __forceinline__ float wave_sum(float x) {
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Workgroup barrier whose fences cover LDS only: it waits for this wave's LDS operations
+// (lgkmcnt) but leaves global loads in flight, so prefetches survive it.
+__device__ __forceinline__ void lds_fence() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
 
 }  // namespace kvp

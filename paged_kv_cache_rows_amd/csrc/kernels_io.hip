@@ -1,7 +1,7 @@
 // Row write into page slots, and the fixed-order merge of split-context partials.
 //
-// Row write: TensorFold PR #1620, opening description, "Writes" bullet (the rows kernel's new
-// K/V rows are copied into the pages).  Merge: the same PR's follow-up discussion, where the
+// Row write: TensorFold PR #1620, opening description, Writes bullet (the K/V rows a layer
+// produces are copied into their page slots).  Merge: the same PR's follow-up discussion, where the
 // tree-attention parts are combined by a merge kernel that reads no pages; here the partials
 // are combined in increasing chunk order, so the result depends only on logical positions.
 #include "internal.h"
@@ -43,49 +43,73 @@ hipError_t launch_rows_put(const RowsArgs &a, hipStream_t st) {
     return hipGetLastError();
 }
 
-// One wave per (stream, row, query head).  Lane c owns channels [c*CPL, (c+1)*CPL).
-template <int CPL>
+// One wave per (stream, row, query head).  Lane = (split group sg, channel block cb): it owns
+// channels [8 cb, 8 cb + 8) of the splits i = sg, sg + SG, ...; the split groups are summed at
+// the end in a fixed order, so the result depends only on the partials, not on timing.
+template <int D>
 __global__ __launch_bounds__(64) void merge_kernel(const MergeArgs a) {
-    const int vec = blockIdx.x;            // (s * R + r) * Hq + h
+    constexpr int CB = D / 8;          // channel blocks of 8
+    constexpr int SG = 64 / CB;        // split groups
+    const int vec = blockIdx.x;        // (s * R + r) * Hq + h
     const int s = vec / (a.R * a.Hq);
     const int r = (vec / a.Hq) % a.R;
     const int L = a.seq_len[s];
     const int lane = threadIdx.x;
-    uint16_t *o = a.out + (size_t)vec * a.D + lane * CPL;
+    const int cb = lane % CB, sg = lane / CB;
     const int pos = L - a.R + r;
-    float res[CPL];
-    for (int c = 0; c < CPL; ++c) res[c] = 0.f;
+    float num[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) num[c] = 0.f;
+    float den = 0.f, M = -INFINITY;
     if (pos >= 0) {
         const int lo = a.window > 0 ? max(0, L - a.R - a.window + 1) : 0;
         const int first = lo / a.chunk;
-        int n = (L + a.chunk - 1) / a.chunk - first;
-        if (n > a.n_splits) n = a.n_splits;
-        const float *ml = a.ws_ml + (size_t)vec * a.n_splits * 2;
-        const float *acc = a.ws_acc + (size_t)vec * a.n_splits * a.D + lane * CPL;
-        float M = -INFINITY;
-        for (int i = 0; i < n; ++i) M = fmaxf(M, ml[2 * i]);
-        float den = 0.f;
-        float num[CPL];
-        for (int c = 0; c < CPL; ++c) num[c] = 0.f;
+        const int n = min((L + a.chunk - 1) / a.chunk - first, a.n_splits);
+        const float2 *ml = reinterpret_cast<const float2 *>(a.ws_ml) + (size_t)vec * a.n_splits;
+        const float *acc = a.ws_acc + (size_t)vec * a.n_splits * D + cb * 8;
+        for (int i = lane; i < n; i += 64) M = fmaxf(M, ml[i].x);
+        M = wave_max(M);
         if (M != -INFINITY) {
-            for (int i = 0; i < n; ++i) {
-                const float mi = ml[2 * i];
-                const float w = (mi == -INFINITY) ? 0.f : fast_exp2(mi - M);
-                den += w * ml[2 * i + 1];
-                const float *ai = acc + (size_t)i * a.D;
+            for (int i0 = 0; i0 < n; i0 += 4 * SG) {
+                float4 x[4][2];
+                float w[4];
 #pragma unroll
-                for (int c = 0; c < CPL; ++c) num[c] += w * ai[c];
+                for (int u = 0; u < 4; ++u) {
+                    const int i = i0 + u * SG + sg;
+                    const bool in = i < n;
+                    const int ic = in ? i : 0;
+                    const float2 m_l = ml[ic];
+                    const float4 *src = reinterpret_cast<const float4 *>(acc + (size_t)ic * D);
+                    x[u][0] = src[0];
+                    x[u][1] = src[1];
+                    w[u] = (in && m_l.x != -INFINITY) ? fast_exp2(m_l.x - M) : 0.f;
+                    if (cb == 0) den += w[u] * m_l.y;
+                }
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    num[0] += w[u] * x[u][0].x; num[1] += w[u] * x[u][0].y;
+                    num[2] += w[u] * x[u][0].z; num[3] += w[u] * x[u][0].w;
+                    num[4] += w[u] * x[u][1].x; num[5] += w[u] * x[u][1].y;
+                    num[6] += w[u] * x[u][1].z; num[7] += w[u] * x[u][1].w;
+                }
             }
         }
-        if (den > 0.f) {
-            const float inv = 1.0f / den;
+    }
+    // sum the split groups (lanes cb, cb + CB, ...) and the denominators (lanes 0, CB, ...)
+    if (SG > 1) {
 #pragma unroll
-            for (int c = 0; c < CPL; ++c) res[c] = num[c] * inv;
+        for (int c = 0; c < 8; ++c) {
+            num[c] = num[c] + __shfl_xor(num[c], 16);
+            if (SG > 2) num[c] = num[c] + __shfl_xor(num[c], 32);
         }
     }
+    den = wave_sum(den);
+    if (sg == 0) {
+        const float inv = den > 0.f ? 1.0f / den : 0.f;
+        uint32_t o[4];
 #pragma unroll
-    for (int c = 0; c < CPL; c += 2) {
-        *reinterpret_cast<uint32_t *>(o + c) = pack_bf16x2(res[c], res[c + 1]);
+        for (int c = 0; c < 4; ++c) o[c] = pack_bf16x2(num[2 * c] * inv, num[2 * c + 1] * inv);
+        *reinterpret_cast<uint4 *>(a.out + (size_t)vec * D + cb * 8) = make_uint4(o[0], o[1], o[2], o[3]);
     }
 }
 
@@ -93,8 +117,8 @@ hipError_t launch_merge(const MergeArgs &a, hipStream_t st) {
     const int blocks = a.S * a.R * a.Hq;
     if (blocks == 0) return hipSuccess;
     switch (a.D) {
-        case 128: hipLaunchKernelGGL(merge_kernel<2>, dim3(blocks), dim3(64), 0, st, a); break;
-        case 512: hipLaunchKernelGGL(merge_kernel<8>, dim3(blocks), dim3(64), 0, st, a); break;
+        case 128: hipLaunchKernelGGL(merge_kernel<128>, dim3(blocks), dim3(64), 0, st, a); break;
+        case 512: hipLaunchKernelGGL(merge_kernel<512>, dim3(blocks), dim3(64), 0, st, a); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

@@ -1,18 +1,20 @@
 // Paged GQA attention part kernel for few query vectors per KV head (rows * group < 16):
 // decode and short verify windows, with VALU bf16 dot products.
 //
-// TensorFold PR #1620 ("Reads" bullet; the author's kernel-timing reply): decode reads keys
+// TensorFold PR #1620 (Reads bullet; the author's kernel-timing reply): decode reads keys
 // through a page table, split over parts of the context that a merge kernel combines, and the
 // page of a tile is looked up once per tile rather than once per key.
 //
 // Design for gfx950 (one wave64 per workgroup; one workgroup per (stream, KV head, chunk)):
 //  * A batch is 16 load instructions per lane of 16 bytes each: 64 keys at D=128 (16 lanes
-//    per row, 4 rows per instruction) or 16 keys at D=512.  When P is a multiple of the batch,
-//    the whole batch lies in one page and the lookup is one scalar table read; otherwise each
-//    lane walks its rows' pages incrementally (no division per key).
+//    per row, 4 rows per instruction) or 16 keys at D=512.  The chunk's page-table entries are
+//    read once into LDS; when P is a multiple of the batch, the whole batch lies in one page
+//    and needs one lookup, otherwise each lane steps through its rows' pages without dividing.
+//  * Loads are unconditional and always land inside the pool (absent pages read page 0), so
+//    no load waits on a branch; V rows outside the chunk are zeroed when staged.
 //  * K and V of a batch go through registers into LDS (rows padded by 16 bytes so that
-//    lane-per-key reads are bank-conflict free); the next batch's loads are in flight while
-//    the current batch is computed.
+//    lane-per-key reads are bank-conflict free); the next batch's loads stay in flight while
+//    the current batch is computed (the barriers fence LDS only).
 //  * QK: one lane per key (D=128) or four lanes per key (D=512, 128 channels each), all G*R
 //    query vectors of the KV head against that key with v_dot2c_f32_bf16, so each K byte is
 //    read from HBM once for the whole GQA group.
@@ -35,15 +37,85 @@ struct ValuGeom {
     static constexpr int SEG = D / QL;        // channels per QK lane
     static constexpr int CHUNK = 16 * NB;     // keys per workgroup
     static constexpr int RS = D + 8;          // LDS row stride (bf16 elements)
+    static constexpr int TC = 72;             // page-table entries cached per chunk
 };
 
 int valu_chunk(int D) { return D == 512 ? ValuGeom<512>::CHUNK : ValuGeom<128>::CHUNK; }
 
-template <int D, int G, int NQ>
+// Loads of one batch (16 rows per lane group, 16 bytes per lane per row).  Every load reads
+// inside the pool: an absent page reads page 0 and an out-of-range row keeps its slot; rows
+// outside the chunk are zeroed later, when V is staged.  The three modes are chosen by a
+// wave-uniform value so that each loop is straight-line code.
+template <int D>
+struct BatchLoader {
+    const uint16_t *k_pages, *v_pages;
+    const int32_t *trow;
+    const int32_t *t_lds;      // page-table entries of the chunk from logical page idx0 on
+    size_t page_elems, head_off;
+    int P, idx0, lrow, ring_pages, stride, num_pages;
+
+    template <int MODE>
+    __device__ __forceinline__ void load(int b, u32x4 (&kr)[16], u32x4 (&vr)[16]) const {
+        constexpr int RPI = ValuGeom<D>::RPI;
+        if constexpr (MODE == 0) {
+            // the whole batch lies in one page: one lookup
+            const int idx = b / P;
+            const int pg = max(t_lds[idx - idx0], 0);
+            const size_t base = (size_t)pg * page_elems + head_off + (size_t)(b - idx * P + lrow) * D;
+#pragma unroll
+            for (int t = 0; t < 16; ++t) {
+                kr[t] = *reinterpret_cast<const u32x4 *>(k_pages + base + (size_t)(t * RPI) * D);
+                vr[t] = *reinterpret_cast<const u32x4 *>(v_pages + base + (size_t)(t * RPI) * D);
+            }
+        } else if constexpr (MODE == 1) {
+            // rows straddle pages: step RPI rows at a time, crossing at most one page boundary
+            const int j0 = b + lrow;
+            int idx = j0 / P;
+            int off = j0 - idx * P;
+#pragma unroll
+            for (int t = 0; t < 16; ++t) {
+                const int pg = max(t_lds[idx - idx0], 0);
+                const size_t e = (size_t)pg * page_elems + head_off + (size_t)off * D;
+                kr[t] = *reinterpret_cast<const u32x4 *>(k_pages + e);
+                vr[t] = *reinterpret_cast<const u32x4 *>(v_pages + e);
+                off += RPI;
+                const bool wrap = off >= P;
+                off = wrap ? off - P : off;
+                idx += wrap ? 1 : 0;
+            }
+        } else {
+            // tiny pages: divide per row and read the table from global memory
+#pragma unroll
+            for (int t = 0; t < 16; ++t) {
+                const int j = b + t * RPI + lrow;
+                int idx = j / P;
+                const int off = j - idx * P;
+                if (ring_pages) idx %= ring_pages;
+                const int tp = trow[min(idx, stride - 1)];
+                const int pg = (idx < stride && (unsigned)tp < (unsigned)num_pages) ? tp : 0;
+                const size_t e = (size_t)pg * page_elems + head_off + (size_t)off * D;
+                kr[t] = *reinterpret_cast<const u32x4 *>(k_pages + e);
+                vr[t] = *reinterpret_cast<const u32x4 *>(v_pages + e);
+            }
+        }
+    }
+};
+
+// Load modes, fixed per launch from P: 0 when P is a multiple of the batch, 1 when rows
+// straddle pages but the chunk's table entries fit the LDS cache, 2 for tiny pages.
+template <int D>
+int valu_mode(int P) {
+    using Geo = ValuGeom<D>;
+    if (P % Geo::NB == 0) return 0;
+    if ((Geo::CHUNK + Geo::NB) / P + 2 <= Geo::TC && Geo::RPI <= P) return 1;
+    return 2;
+}
+
+template <int D, int G, int NQ, int MODE>
 __global__ __launch_bounds__(64) void part_valu_kernel(const PartArgs a) {
     using Geo = ValuGeom<D>;
     constexpr int LPR = Geo::LPR, RPI = Geo::RPI, NB = Geo::NB, QL = Geo::QL, SEG = Geo::SEG;
-    constexpr int CHUNK = Geo::CHUNK, RS = Geo::RS;
+    constexpr int CHUNK = Geo::CHUNK, RS = Geo::RS, TC = Geo::TC;
     constexpr int R = NQ / G;
     static_assert(NQ % G == 0 && NQ % 4 == 0, "query vectors come in whole rows of 4 or 8");
 
@@ -51,6 +123,7 @@ __global__ __launch_bounds__(64) void part_valu_kernel(const PartArgs a) {
     __shared__ __attribute__((aligned(16))) uint16_t v_lds[NB * RS];
     __shared__ __attribute__((aligned(16))) uint16_t q_lds[NQ * RS];
     __shared__ __attribute__((aligned(16))) uint32_t p_lds[(NB / 2) * NQ];
+    __shared__ int32_t t_lds[TC];
 
     const int lane = threadIdx.x;
     const int split = blockIdx.x, kvh = blockIdx.y, s = blockIdx.z;
@@ -71,53 +144,35 @@ __global__ __launch_bounds__(64) void part_valu_kernel(const PartArgs a) {
         *reinterpret_cast<uint4 *>(q_lds + v * RS + c * 8) = *src;
     }
 
+    const uint16_t *q_rows[NQ];
+#pragma unroll
+    for (int v = 0; v < NQ; ++v)
+        q_rows[v] = a.q + ((size_t)(s * R + v / G) * a.Hq + kvh * G + (v % G)) * D;
+
     const int lrow = lane / LPR;            // row inside a group of RPI rows (load and PV)
     const int lch = lane - lrow * LPR;      // 16-byte piece of the row
     const size_t page_elems = (size_t)a.Hkv * a.P * D;
     const size_t head_off = (size_t)kvh * a.P * D + (size_t)lch * 8;
     const int32_t *trow = a.table + (size_t)s * a.stride;
-    const bool one_page_per_batch = (a.P % NB) == 0;
+    const int P = a.P;
+    const int b_first = (kbeg / NB) * NB;
 
-    uint4 kr[16], vr[16];
-    auto load_batch = [&](int b) {
-        if (one_page_per_batch) {
-            int idx = b / a.P;
-            const int off0 = b - idx * a.P;
+    // The chunk's page-table entries, looked up once per chunk into LDS (logical page index
+    // idx0 + i); entries past the table or outside the pool become -1.
+    const int idx0 = b_first / P;
+    if (MODE != 2) {
+        for (int i = lane; i < TC; i += 64) {
+            int idx = idx0 + i;
             if (a.ring_pages) idx %= a.ring_pages;
-            const int pg = idx < a.stride ? trow[idx] : -1;
-            const bool page_ok = (unsigned)pg < (unsigned)a.num_pages;
-            const size_t base = (size_t)(page_ok ? pg : 0) * page_elems + head_off + (size_t)(off0 + lrow) * D;
-#pragma unroll
-            for (int t = 0; t < 16; ++t) {
-                const int j = b + t * RPI + lrow;
-                const bool in = page_ok && j >= kbeg && j < kend;
-                const size_t e = base + (size_t)(t * RPI) * D;
-                kr[t] = in ? *reinterpret_cast<const uint4 *>(a.k_pages + e) : make_uint4(0, 0, 0, 0);
-                vr[t] = in ? *reinterpret_cast<const uint4 *>(a.v_pages + e) : make_uint4(0, 0, 0, 0);
-            }
-        } else {
-            const int j0 = b + lrow;
-            int idx = j0 / a.P;
-            int off = j0 - idx * a.P;
-            if (a.ring_pages) idx %= a.ring_pages;
-#pragma unroll
-            for (int t = 0; t < 16; ++t) {
-                const int j = j0 + t * RPI;
-                bool in = j >= kbeg && j < kend && idx < a.stride;
-                const int pg = in ? trow[idx] : -1;
-                in = in && (unsigned)pg < (unsigned)a.num_pages;
-                const size_t e = (size_t)(in ? pg : 0) * page_elems + head_off + (size_t)off * D;
-                kr[t] = in ? *reinterpret_cast<const uint4 *>(a.k_pages + e) : make_uint4(0, 0, 0, 0);
-                vr[t] = in ? *reinterpret_cast<const uint4 *>(a.v_pages + e) : make_uint4(0, 0, 0, 0);
-                off += RPI;
-                while (off >= a.P) {
-                    off -= a.P;
-                    ++idx;
-                    if (a.ring_pages && idx == a.ring_pages) idx = 0;
-                }
-            }
+            int pg = -1;
+            if (idx < a.stride) pg = trow[idx];
+            t_lds[i] = ((unsigned)pg < (unsigned)a.num_pages) ? pg : -1;
         }
-    };
+    }
+    lds_fence();
+    BatchLoader<D> ld{a.k_pages, a.v_pages, trow, t_lds, page_elems, head_off, P, idx0, lrow,
+                      a.ring_pages, a.stride, a.num_pages};
+    u32x4 kr[16], vr[16];
 
     float m_run[NQ], l_run[NQ], acc[NQ][8];
 #pragma unroll
@@ -128,23 +183,34 @@ __global__ __launch_bounds__(64) void part_valu_kernel(const PartArgs a) {
         for (int c = 0; c < 8; ++c) acc[v][c] = 0.f;
     }
 
-    const int b_first = (kbeg / NB) * NB;
     const int nb = (kend - b_first + NB - 1) / NB;
     const int kk = (QL == 1) ? lane : (lane % NB);     // key of this lane in the QK stage
     const int seg = (QL == 1) ? 0 : (lane / NB);       // its channel segment
     const float scale_log2 = a.scale_log2;
 
-    load_batch(b_first);
+    ld.template load<MODE>(b_first, kr, vr);
     for (int ib = 0; ib < nb; ++ib) {
         const int b = b_first + ib * NB;
-        __syncthreads();
+        lds_fence();
 #pragma unroll
-        for (int t = 0; t < 16; ++t) {
-            *reinterpret_cast<uint4 *>(k_lds + (t * RPI + lrow) * RS + lch * 8) = kr[t];
-            *reinterpret_cast<uint4 *>(v_lds + (t * RPI + lrow) * RS + lch * 8) = vr[t];
+        for (int t = 0; t < 16; ++t)
+            *reinterpret_cast<u32x4 *>(k_lds + (t * RPI + lrow) * RS + lch * 8) = kr[t];
+        if (b >= kbeg && b + NB <= kend) {
+#pragma unroll
+            for (int t = 0; t < 16; ++t)
+                *reinterpret_cast<u32x4 *>(v_lds + (t * RPI + lrow) * RS + lch * 8) = vr[t];
+        } else {
+            // a batch at the chunk's edge: V rows outside [kbeg, kend) become zeros, so that a
+            // zero weight never meets a NaN in an unused slot
+#pragma unroll
+            for (int t = 0; t < 16; ++t) {
+                const int j = b + t * RPI + lrow;
+                const uint32_t keep = (j >= kbeg && j < kend) ? 0xFFFFFFFFu : 0u;
+                *reinterpret_cast<u32x4 *>(v_lds + (t * RPI + lrow) * RS + lch * 8) = vr[t] & keep;
+            }
         }
-        if (ib + 1 < nb) load_batch(b + NB);
-        __syncthreads();
+        if (ib + 1 < nb) ld.template load<MODE>(b + NB, kr, vr);
+        lds_fence();
 
         // ---- scores: this lane's key against every query vector of the KV head
         float sc[NQ];
@@ -157,7 +223,10 @@ __global__ __launch_bounds__(64) void part_valu_kernel(const PartArgs a) {
             const uint4 kv = *reinterpret_cast<const uint4 *>(krow + cb * 8);
 #pragma unroll
             for (int v = 0; v < NQ; ++v) {
-                const uint4 qv = *reinterpret_cast<const uint4 *>(qb + v * RS + cb * 8);
+                // one lane per key: the query is wave-uniform and read through the scalar cache
+                // into SGPRs; with four lanes per key each lane reads its segment from LDS
+                const uint4 qv = (QL == 1) ? *reinterpret_cast<const uint4 *>(q_rows[v] + cb * 8)
+                                           : *reinterpret_cast<const uint4 *>(qb + v * RS + cb * 8);
                 float x = sc[v];
                 x = dot2_bf16(qv.x, kv.x, x);
                 x = dot2_bf16(qv.y, kv.y, x);
@@ -213,7 +282,7 @@ __global__ __launch_bounds__(64) void part_valu_kernel(const PartArgs a) {
 #pragma unroll
                 for (int c = 0; c < 8; ++c) acc[v][c] *= alpha[v];
         }
-        __syncthreads();
+        lds_fence();
 
         // ---- PV: lane owns channels lch*8..+8 of keys t*RPI + lrow
 #pragma unroll
@@ -276,7 +345,12 @@ bool valu_supported(int D, int G, int NQ) {
 
 template <int D, int G, int NQ>
 static hipError_t launch_one(const PartArgs &a, int S, hipStream_t st) {
-    hipLaunchKernelGGL((part_valu_kernel<D, G, NQ>), dim3(a.n_splits, a.Hkv, S), dim3(64), 0, st, a);
+    const dim3 grid(a.n_splits, a.Hkv, S);
+    switch (valu_mode<D>(a.P)) {
+        case 0: hipLaunchKernelGGL((part_valu_kernel<D, G, NQ, 0>), grid, dim3(64), 0, st, a); break;
+        case 1: hipLaunchKernelGGL((part_valu_kernel<D, G, NQ, 1>), grid, dim3(64), 0, st, a); break;
+        default: hipLaunchKernelGGL((part_valu_kernel<D, G, NQ, 2>), grid, dim3(64), 0, st, a); break;
+    }
     return hipGetLastError();
 }
 
