@@ -62,22 +62,28 @@ __global__ __launch_bounds__(64) void merge_kernel(const MergeArgs a) {
     for (int c = 0; c < 8; ++c) num[c] = 0.f;
     float den = 0.f, M = -INFINITY;
     if (pos >= 0) {
-        const int lo = a.window > 0 ? max(0, L - a.R - a.window + 1) : 0;
-        const int first = lo / a.chunk;
-        const int n = min((L + a.chunk - 1) / a.chunk - first, a.n_splits);
+        // splits are chunks counted from the first chunk any row of the stream sees; this row
+        // reads only the chunks holding its own keys [lo_r, pos]
+        const int lo_stream = a.window > 0 ? max(0, L - a.R - a.window + 1) : 0;
+        const int lo_r = a.window > 0 ? max(0, pos - a.window + 1) : 0;
+        const int first = lo_stream / a.chunk;
+        const int i_begin = lo_r / a.chunk - first;
+        const int n = min(pos / a.chunk - first + 1, a.n_splits);
         const float2 *ml = reinterpret_cast<const float2 *>(a.ws_ml) + (size_t)vec * a.n_splits;
         const float *acc = a.ws_acc + (size_t)vec * a.n_splits * D + cb * 8;
-        for (int i = lane; i < n; i += 64) M = fmaxf(M, ml[i].x);
+        for (int i = i_begin + lane; i < n; i += 64) M = fmaxf(M, ml[i].x);
         M = wave_max(M);
         if (M != -INFINITY) {
-            for (int i0 = 0; i0 < n; i0 += 4 * SG) {
+            for (int i0 = i_begin; i0 < n; i0 += 4 * SG) {
                 float4 x[4][2];
                 float w[4];
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
                     const int i = i0 + u * SG + sg;
                     const bool in = i < n;
-                    const int ic = in ? i : 0;
+                    // a padded slot rereads the row's first split, which is always written
+                    // (a zero weight must never meet an unwritten, possibly NaN, split)
+                    const int ic = in ? i : i_begin;
                     const float2 m_l = ml[ic];
                     const float4 *src = reinterpret_cast<const float4 *>(acc + (size_t)ic * D);
                     x[u][0] = src[0];
