@@ -76,6 +76,13 @@ __device__ __forceinline__ float wave_sum(float x) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Orders this wave's LDS accesses for the compiler without emitting any wait: within one wave
+// the LDS unit executes DS instructions in issue order, so data exchanged between the lanes of
+// one wave through LDS needs no barrier, only that the compiler keep the order.
+__device__ __forceinline__ void wave_lds_fence() {
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront", "local");
+}
+
 // Workgroup barrier whose fences cover LDS only: it waits for this wave's LDS operations
 // (lgkmcnt) but leaves global loads in flight, so prefetches survive it.
 __device__ __forceinline__ void lds_fence() {

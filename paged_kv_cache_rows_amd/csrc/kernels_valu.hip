@@ -42,42 +42,47 @@ struct ValuGeom {
 
 int valu_chunk(int D) { return D == 512 ? ValuGeom<512>::CHUNK : ValuGeom<128>::CHUNK; }
 
-// Loads of one batch (16 rows per lane group, 16 bytes per lane per row).  Every load reads
-// inside the pool: an absent page reads page 0 and an out-of-range row keeps its slot; rows
-// outside the chunk are zeroed later, when V is staged.  The three modes are chosen by a
-// wave-uniform value so that each loop is straight-line code.
-template <int D>
+// Loads of one batch.  A batch is 16 load slots t per operand; slot t is rows t*RPI .. +RPI-1
+// (16 bytes per lane).  Wave w owns the contiguous slots [w*NS, w*NS + NS) (NS even, so both
+// keys of a PV pair (2 tp, 2 tp + 1) are loaded by one wave).  Every load reads inside the
+// pool: an absent page reads page 0 and an out-of-range row keeps its slot; rows outside the
+// chunk are zeroed when V is staged.  MODE is fixed per launch from P so that each loop is
+// straight-line code.
+template <int D, int NW>
 struct BatchLoader {
+    static constexpr int NS = ((16 + NW - 1) / NW + 1) / 2 * 2;   // slots per wave (even)
     const uint16_t *k_pages, *v_pages;
     const int32_t *trow;
     const int32_t *t_lds;      // page-table entries of the chunk from logical page idx0 on
     size_t page_elems, head_off;
-    int P, idx0, lrow, ring_pages, stride, num_pages;
+    int P, idx0, lrow, wave, ring_pages, stride, num_pages;
 
     template <int MODE>
-    __device__ __forceinline__ void load(int b, u32x4 (&kr)[16], u32x4 (&vr)[16]) const {
+    __device__ __forceinline__ void load(int b, u32x4 (&kr)[NS], u32x4 (&vr)[NS]) const {
         constexpr int RPI = ValuGeom<D>::RPI;
+        const int t0 = wave * NS;
         if constexpr (MODE == 0) {
             // the whole batch lies in one page: one lookup
             const int idx = b / P;
             const int pg = max(t_lds[idx - idx0], 0);
             const size_t base = (size_t)pg * page_elems + head_off + (size_t)(b - idx * P + lrow) * D;
 #pragma unroll
-            for (int t = 0; t < 16; ++t) {
-                kr[t] = *reinterpret_cast<const u32x4 *>(k_pages + base + (size_t)(t * RPI) * D);
-                vr[t] = *reinterpret_cast<const u32x4 *>(v_pages + base + (size_t)(t * RPI) * D);
+            for (int i = 0; i < NS; ++i) {
+                const int t = min(t0 + i, 15);
+                kr[i] = *reinterpret_cast<const u32x4 *>(k_pages + base + (size_t)(t * RPI) * D);
+                vr[i] = *reinterpret_cast<const u32x4 *>(v_pages + base + (size_t)(t * RPI) * D);
             }
         } else if constexpr (MODE == 1) {
-            // rows straddle pages: step RPI rows at a time, crossing at most one page boundary
-            const int j0 = b + lrow;
+            // rows straddle pages: step RPI rows at a time, crossing at most one boundary
+            const int j0 = b + t0 * RPI + lrow;
             int idx = j0 / P;
             int off = j0 - idx * P;
 #pragma unroll
-            for (int t = 0; t < 16; ++t) {
+            for (int i = 0; i < NS; ++i) {
                 const int pg = max(t_lds[idx - idx0], 0);
                 const size_t e = (size_t)pg * page_elems + head_off + (size_t)off * D;
-                kr[t] = *reinterpret_cast<const u32x4 *>(k_pages + e);
-                vr[t] = *reinterpret_cast<const u32x4 *>(v_pages + e);
+                kr[i] = *reinterpret_cast<const u32x4 *>(k_pages + e);
+                vr[i] = *reinterpret_cast<const u32x4 *>(v_pages + e);
                 off += RPI;
                 const bool wrap = off >= P;
                 off = wrap ? off - P : off;
@@ -86,7 +91,8 @@ struct BatchLoader {
         } else {
             // tiny pages: divide per row and read the table from global memory
 #pragma unroll
-            for (int t = 0; t < 16; ++t) {
+            for (int i = 0; i < NS; ++i) {
+                const int t = min(t0 + i, 15);
                 const int j = b + t * RPI + lrow;
                 int idx = j / P;
                 const int off = j - idx * P;
@@ -94,12 +100,18 @@ struct BatchLoader {
                 const int tp = trow[min(idx, stride - 1)];
                 const int pg = (idx < stride && (unsigned)tp < (unsigned)num_pages) ? tp : 0;
                 const size_t e = (size_t)pg * page_elems + head_off + (size_t)off * D;
-                kr[t] = *reinterpret_cast<const u32x4 *>(k_pages + e);
-                vr[t] = *reinterpret_cast<const u32x4 *>(v_pages + e);
+                kr[i] = *reinterpret_cast<const u32x4 *>(k_pages + e);
+                vr[i] = *reinterpret_cast<const u32x4 *>(v_pages + e);
             }
         }
     }
 };
+
+// Query vectors per wave (VW) and waves per workgroup (NW = NQ / VW).
+template <int NQ>
+constexpr int valu_vw() { return NQ % 2 == 0 && NQ <= 8 ? 2 : 4; }
+template <int NQ>
+constexpr int valu_waves() { return NQ / valu_vw<NQ>(); }
 
 // Load modes, fixed per launch from P: 0 when P is a multiple of the batch, 1 when rows
 // straddle pages but the chunk's table entries fit the LDS cache, 2 for tiny pages.
@@ -112,20 +124,29 @@ int valu_mode(int P) {
 }
 
 template <int D, int G, int NQ, int MODE>
-__global__ __launch_bounds__(64) void part_valu_kernel(const PartArgs a) {
+__global__ __launch_bounds__(64 * valu_waves<NQ>()) void part_valu_kernel(const PartArgs a) {
     using Geo = ValuGeom<D>;
     constexpr int LPR = Geo::LPR, RPI = Geo::RPI, NB = Geo::NB, QL = Geo::QL, SEG = Geo::SEG;
     constexpr int CHUNK = Geo::CHUNK, RS = Geo::RS, TC = Geo::TC;
     constexpr int R = NQ / G;
-    static_assert(NQ % G == 0 && NQ % 4 == 0, "query vectors come in whole rows of 4 or 8");
+    constexpr int VW = valu_vw<NQ>();                   // query vectors per wave
+    constexpr int NW = valu_waves<NQ>();
+    using Loader = BatchLoader<D, NW>;
+    constexpr int NS = Loader::NS;
+    constexpr int PRS = 2 * D + 16;                     // V pair-row stride (bf16 elements)
+    static_assert(NQ % G == 0 && NQ % VW == 0, "query vectors split evenly over the waves");
 
+    // K tile (row-major, rows padded by 16 bytes for conflict-free lane-per-key reads), V tile
+    // as key pairs (pair row pr = tp*RPI + lrow holds, per channel, the two keys 2tp*RPI + lrow
+    // and (2tp+1)*RPI + lrow packed as one bf16x2 word), queries, weights, page table.
     __shared__ __attribute__((aligned(16))) uint16_t k_lds[NB * RS];
-    __shared__ __attribute__((aligned(16))) uint16_t v_lds[NB * RS];
+    __shared__ __attribute__((aligned(16))) uint16_t v_lds[(NB / 2) * PRS];
     __shared__ __attribute__((aligned(16))) uint16_t q_lds[NQ * RS];
-    __shared__ __attribute__((aligned(16))) uint32_t p_lds[(NB / 2) * NQ];
+    __shared__ __attribute__((aligned(16))) uint32_t p_lds[NW][(NB / 2) * VW];
     __shared__ int32_t t_lds[TC];
 
-    const int lane = threadIdx.x;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
     const int split = blockIdx.x, kvh = blockIdx.y, s = blockIdx.z;
     const int L = a.seq_len[s];
     const int W = a.window;
@@ -135,19 +156,13 @@ __global__ __launch_bounds__(64) void part_valu_kernel(const PartArgs a) {
     const int kbeg = max(c0, lo);
     const int kend = min(c0 + CHUNK, L);
 
-    // Queries of this KV head: vector v = r * G + g is row r, query head kvh * G + g.
-    for (int i = lane; i < NQ * (D / 8); i += 64) {
+    // All query vectors of this KV head into LDS: vector v is row v / G, query head kvh*G + v%G.
+    // Wave w computes vectors [VW*w, VW*w + VW).
+    for (int i = tid; i < NQ * (D / 8); i += 64 * NW) {
         const int v = i / (D / 8), c = i - (i / (D / 8)) * (D / 8);
-        const int r = v / G, g = v - (v / G) * G;
-        const uint4 *src = reinterpret_cast<const uint4 *>(
-            a.q + ((size_t)(s * R + r) * a.Hq + kvh * G + g) * D) + c;
-        *reinterpret_cast<uint4 *>(q_lds + v * RS + c * 8) = *src;
+        *reinterpret_cast<u32x4 *>(q_lds + v * RS + c * 8) =
+            *reinterpret_cast<const u32x4 *>(a.q + ((size_t)(s * R + v / G) * a.Hq + kvh * G + (v % G)) * D + c * 8);
     }
-
-    const uint16_t *q_rows[NQ];
-#pragma unroll
-    for (int v = 0; v < NQ; ++v)
-        q_rows[v] = a.q + ((size_t)(s * R + v / G) * a.Hq + kvh * G + (v % G)) * D;
 
     const int lrow = lane / LPR;            // row inside a group of RPI rows (load and PV)
     const int lch = lane - lrow * LPR;      // 16-byte piece of the row
@@ -161,7 +176,7 @@ __global__ __launch_bounds__(64) void part_valu_kernel(const PartArgs a) {
     // idx0 + i); entries past the table or outside the pool become -1.
     const int idx0 = b_first / P;
     if (MODE != 2) {
-        for (int i = lane; i < TC; i += 64) {
+        for (int i = tid; i < TC; i += 64 * NW) {
             int idx = idx0 + i;
             if (a.ring_pages) idx %= a.ring_pages;
             int pg = -1;
@@ -170,13 +185,13 @@ __global__ __launch_bounds__(64) void part_valu_kernel(const PartArgs a) {
         }
     }
     lds_fence();
-    BatchLoader<D> ld{a.k_pages, a.v_pages, trow, t_lds, page_elems, head_off, P, idx0, lrow,
-                      a.ring_pages, a.stride, a.num_pages};
-    u32x4 kr[16], vr[16];
+    const Loader ld{a.k_pages, a.v_pages, trow, t_lds, page_elems, head_off, P, idx0, lrow, wave,
+                    a.ring_pages, a.stride, a.num_pages};
+    u32x4 kr[NS], vr[NS];
 
-    float m_run[NQ], l_run[NQ], acc[NQ][8];
+    float m_run[VW], l_run[VW], acc[VW][8];
 #pragma unroll
-    for (int v = 0; v < NQ; ++v) {
+    for (int v = 0; v < VW; ++v) {
         m_run[v] = -INFINITY;
         l_run[v] = 0.f;
 #pragma unroll
@@ -187,46 +202,53 @@ __global__ __launch_bounds__(64) void part_valu_kernel(const PartArgs a) {
     const int kk = (QL == 1) ? lane : (lane % NB);     // key of this lane in the QK stage
     const int seg = (QL == 1) ? 0 : (lane / NB);       // its channel segment
     const float scale_log2 = a.scale_log2;
+    // keys every row of the call sees: up to row 0's own position, and inside every window
+    const int all_hi = L - R + 1;
+    const int all_lo = W > 0 ? L - W : 0;
+    uint32_t *p_mine = p_lds[wave];
+    const uint16_t *qb = q_lds + (VW * wave) * RS + seg * SEG;
 
     ld.template load<MODE>(b_first, kr, vr);
     for (int ib = 0; ib < nb; ++ib) {
         const int b = b_first + ib * NB;
-        lds_fence();
+        lds_fence();                        // every wave is done with the previous tiles
+        const bool inside = b >= kbeg && b + NB <= kend;
 #pragma unroll
-        for (int t = 0; t < 16; ++t)
-            *reinterpret_cast<u32x4 *>(k_lds + (t * RPI + lrow) * RS + lch * 8) = kr[t];
-        if (b >= kbeg && b + NB <= kend) {
-#pragma unroll
-            for (int t = 0; t < 16; ++t)
-                *reinterpret_cast<u32x4 *>(v_lds + (t * RPI + lrow) * RS + lch * 8) = vr[t];
-        } else {
-            // a batch at the chunk's edge: V rows outside [kbeg, kend) become zeros, so that a
-            // zero weight never meets a NaN in an unused slot
-#pragma unroll
-            for (int t = 0; t < 16; ++t) {
-                const int j = b + t * RPI + lrow;
-                const uint32_t keep = (j >= kbeg && j < kend) ? 0xFFFFFFFFu : 0u;
-                *reinterpret_cast<u32x4 *>(v_lds + (t * RPI + lrow) * RS + lch * 8) = vr[t] & keep;
+        for (int i = 0; i < NS; i += 2) {
+            const int t = wave * NS + i;
+            if (NS * NW == 16 || t < 16) {
+                const int row0 = t * RPI + lrow, row1 = row0 + RPI;
+                *reinterpret_cast<u32x4 *>(k_lds + row0 * RS + lch * 8) = kr[i];
+                *reinterpret_cast<u32x4 *>(k_lds + row1 * RS + lch * 8) = kr[i + 1];
+                // at the chunk's edges, V rows outside it become zeros, so that a zero weight
+                // never meets a NaN in an unused slot
+                const uint32_t k0 = (inside || (b + row0 >= kbeg && b + row0 < kend)) ? 0xFFFFFFFFu : 0u;
+                const uint32_t k1 = (inside || (b + row1 >= kbeg && b + row1 < kend)) ? 0xFFFFFFFFu : 0u;
+                const u32x4 va = vr[i] & k0, vb = vr[i + 1] & k1;
+                // interleave the pair: word c holds channel c of both keys
+                const u32x4 p0 = u32x4{(va.x & 0xFFFFu) | (vb.x << 16), (va.x >> 16) | (vb.x & 0xFFFF0000u),
+                                       (va.y & 0xFFFFu) | (vb.y << 16), (va.y >> 16) | (vb.y & 0xFFFF0000u)};
+                const u32x4 p1 = u32x4{(va.z & 0xFFFFu) | (vb.z << 16), (va.z >> 16) | (vb.z & 0xFFFF0000u),
+                                       (va.w & 0xFFFFu) | (vb.w << 16), (va.w >> 16) | (vb.w & 0xFFFF0000u)};
+                uint16_t *dst = v_lds + ((t / 2) * RPI + lrow) * PRS + lch * 16;
+                *reinterpret_cast<u32x4 *>(dst) = p0;
+                *reinterpret_cast<u32x4 *>(dst + 8) = p1;
             }
         }
-        if (ib + 1 < nb) ld.template load<MODE>(b + NB, kr, vr);
+        if (ib + 1 < nb) ld.template load<MODE>(b + NB, kr, vr);     // a full batch ahead
         lds_fence();
 
-        // ---- scores: this lane's key against every query vector of the KV head
-        float sc[NQ];
+        // ---- scores: this lane's key against this wave's query vectors
+        float sc[VW];
 #pragma unroll
-        for (int v = 0; v < NQ; ++v) sc[v] = 0.f;
+        for (int v = 0; v < VW; ++v) sc[v] = 0.f;
         const uint16_t *krow = k_lds + kk * RS + seg * SEG;
-        const uint16_t *qb = q_lds + seg * SEG;
 #pragma unroll
         for (int cb = 0; cb < SEG / 8; ++cb) {
-            const uint4 kv = *reinterpret_cast<const uint4 *>(krow + cb * 8);
+            const u32x4 kv = *reinterpret_cast<const u32x4 *>(krow + cb * 8);
 #pragma unroll
-            for (int v = 0; v < NQ; ++v) {
-                // one lane per key: the query is wave-uniform and read through the scalar cache
-                // into SGPRs; with four lanes per key each lane reads its segment from LDS
-                const uint4 qv = (QL == 1) ? *reinterpret_cast<const uint4 *>(q_rows[v] + cb * 8)
-                                           : *reinterpret_cast<const uint4 *>(qb + v * RS + cb * 8);
+            for (int v = 0; v < VW; ++v) {
+                const u32x4 qv = *reinterpret_cast<const u32x4 *>(qb + v * RS + cb * 8);
                 float x = sc[v];
                 x = dot2_bf16(qv.x, kv.x, x);
                 x = dot2_bf16(qv.y, kv.y, x);
@@ -237,87 +259,96 @@ __global__ __launch_bounds__(64) void part_valu_kernel(const PartArgs a) {
         }
         if (QL > 1) {
 #pragma unroll
-            for (int v = 0; v < NQ; ++v) {
+            for (int v = 0; v < VW; ++v) {
                 sc[v] = sc[v] + __shfl_xor(sc[v], 16);
                 sc[v] = sc[v] + __shfl_xor(sc[v], 32);
             }
         }
 
-        // ---- online softmax (log2 domain)
-        const int j = b + kk;
-        float pv[NQ], alpha[NQ];
-        bool rescale = false;
+        // ---- online softmax (log2 domain).  A batch that every row sees whole needs no mask;
+        // otherwise masked keys are selected out (never multiplied by zero).
+        float x[VW];
+        if (inside && b + NB <= all_hi && b >= all_lo) {
 #pragma unroll
-        for (int v = 0; v < NQ; ++v) {
-            const int pr = L - R + v / G;                 // position of this vector's row
-            const int lor = W > 0 ? pr - W + 1 : 0;
-            const bool vis = j >= kbeg && j < kend && j <= pr && j >= lor;
-            const float x = vis ? sc[v] * scale_log2 : -INFINITY;
-            const float bm = wave_max(x);
-            const float mn = fmaxf(m_run[v], bm);
-            const float al = (mn == -INFINITY) ? 1.f : fast_exp2(m_run[v] - mn);
-            pv[v] = vis ? fast_exp2(x - mn) : 0.f;
-            m_run[v] = mn;
-            alpha[v] = al;
-            rescale |= (al != 1.f);
-            l_run[v] = l_run[v] * al + (seg == 0 ? pv[v] : 0.f);
+            for (int v = 0; v < VW; ++v) x[v] = sc[v] * scale_log2;
+        } else {
+            const int j = b + kk;
+#pragma unroll
+            for (int v = 0; v < VW; ++v) {
+                const int pr = L - R + (VW * wave + v) / G;   // position of this vector's row
+                const int lor = W > 0 ? pr - W + 1 : 0;
+                const bool vis = j >= kbeg && j < kend && j <= pr && j >= lor;
+                x[v] = vis ? sc[v] * scale_log2 : -INFINITY;
+            }
+        }
+        // The running max moves only when a score of the batch exceeds it (rare after the first
+        // batches); only then are the wave maxima reduced and the sums rescaled.
+        uint64_t over = 0;
+#pragma unroll
+        for (int v = 0; v < VW; ++v) over |= __builtin_amdgcn_ballot_w64(x[v] > m_run[v]);
+        if (over) {
+#pragma unroll
+            for (int v = 0; v < VW; ++v) {
+                const float mn = fmaxf(m_run[v], wave_max(x[v]));
+                const float al = (mn == -INFINITY) ? 1.f : fast_exp2(m_run[v] - mn);
+                m_run[v] = mn;
+                l_run[v] *= al;
+#pragma unroll
+                for (int c = 0; c < 8; ++c) acc[v][c] *= al;
+            }
+        }
+        float pv[VW];
+#pragma unroll
+        for (int v = 0; v < VW; ++v) {
+            pv[v] = (x[v] == -INFINITY) ? 0.f : fast_exp2(x[v] - m_run[v]);
+            l_run[v] += (seg == 0) ? pv[v] : 0.f;
         }
         // pack (p[key], p[key + RPI]) as bf16 pairs for the PV dot2
-        const bool writer = seg == 0 && ((kk / RPI) & 1) == 0;
-        const int pid = (kk / (2 * RPI)) * RPI + (kk % RPI);
+        {
+            uint32_t w[VW];
 #pragma unroll
-        for (int v4 = 0; v4 < NQ / 4; ++v4) {
-            uint32_t w[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float partner = __shfl_down(pv[v4 * 4 + i], RPI);
-                w[i] = pack_bf16x2(pv[v4 * 4 + i], partner);
+            for (int v = 0; v < VW; ++v) w[v] = pack_bf16x2(pv[v], __shfl_down(pv[v], RPI));
+            const bool writer = seg == 0 && ((kk / RPI) & 1) == 0;
+            const int pid = (kk / (2 * RPI)) * RPI + (kk % RPI);
+            if (writer) {
+                if constexpr (VW == 4)
+                    *reinterpret_cast<u32x4 *>(p_mine + pid * VW) = u32x4{w[0], w[1], w[2], w[3]};
+                else
+                    *reinterpret_cast<uint2 *>(p_mine + pid * VW) = make_uint2(w[0], w[1]);
             }
-            if (writer)
-                *reinterpret_cast<uint4 *>(p_lds + pid * NQ + v4 * 4) = make_uint4(w[0], w[1], w[2], w[3]);
         }
-        if (rescale) {
-#pragma unroll
-            for (int v = 0; v < NQ; ++v)
-#pragma unroll
-                for (int c = 0; c < 8; ++c) acc[v][c] *= alpha[v];
-        }
-        lds_fence();
+        wave_lds_fence();
 
-        // ---- PV: lane owns channels lch*8..+8 of keys t*RPI + lrow
+        // ---- PV: lane owns channels lch*8..+8 of the key pairs (2tp*RPI + lrow, +RPI)
 #pragma unroll
         for (int tp = 0; tp < 8; ++tp) {
-            const uint4 va = *reinterpret_cast<const uint4 *>(v_lds + ((2 * tp) * RPI + lrow) * RS + lch * 8);
-            const uint4 vb = *reinterpret_cast<const uint4 *>(v_lds + ((2 * tp + 1) * RPI + lrow) * RS + lch * 8);
-            uint32_t vp[8];
-            vp[0] = (va.x & 0xFFFFu) | (vb.x << 16);
-            vp[1] = (va.x >> 16) | (vb.x & 0xFFFF0000u);
-            vp[2] = (va.y & 0xFFFFu) | (vb.y << 16);
-            vp[3] = (va.y >> 16) | (vb.y & 0xFFFF0000u);
-            vp[4] = (va.z & 0xFFFFu) | (vb.z << 16);
-            vp[5] = (va.z >> 16) | (vb.z & 0xFFFF0000u);
-            vp[6] = (va.w & 0xFFFFu) | (vb.w << 16);
-            vp[7] = (va.w >> 16) | (vb.w & 0xFFFF0000u);
-            const int prd = tp * RPI + lrow;
-#pragma unroll
-            for (int v4 = 0; v4 < NQ / 4; ++v4) {
-                const uint4 pp = *reinterpret_cast<const uint4 *>(p_lds + prd * NQ + v4 * 4);
-                const uint32_t pw[4] = {pp.x, pp.y, pp.z, pp.w};
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-#pragma unroll
-                    for (int c = 0; c < 8; ++c) acc[v4 * 4 + i][c] = dot2_bf16(pw[i], vp[c], acc[v4 * 4 + i][c]);
+            const int pr = tp * RPI + lrow;
+            const uint16_t *src = v_lds + pr * PRS + lch * 16;
+            const u32x4 p0 = *reinterpret_cast<const u32x4 *>(src);
+            const u32x4 p1 = *reinterpret_cast<const u32x4 *>(src + 8);
+            const uint32_t vp[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+            uint32_t pw[VW];
+            if constexpr (VW == 4) {
+                const u32x4 pp = *reinterpret_cast<const u32x4 *>(p_mine + pr * VW);
+                pw[0] = pp.x; pw[1] = pp.y; pw[2] = pp.z; pw[3] = pp.w;
+            } else {
+                const uint2 pp = *reinterpret_cast<const uint2 *>(p_mine + pr * VW);
+                pw[0] = pp.x; pw[1] = pp.y;
             }
+#pragma unroll
+            for (int v = 0; v < VW; ++v)
+#pragma unroll
+                for (int c = 0; c < 8; ++c) acc[v][c] = dot2_bf16(pw[v], vp[c], acc[v][c]);
         }
     }
 
-    // ---- epilogue: combine lanes, write the partial of this chunk
-    float l_tot[NQ];
+    // ---- epilogue: combine lanes, write this wave's partials of the chunk
+    float l_tot[VW];
 #pragma unroll
-    for (int v = 0; v < NQ; ++v) l_tot[v] = wave_sum(l_run[v]);
+    for (int v = 0; v < VW; ++v) l_tot[v] = wave_sum(l_run[v]);
     if (RPI > 1) {
 #pragma unroll
-        for (int v = 0; v < NQ; ++v)
+        for (int v = 0; v < VW; ++v)
 #pragma unroll
             for (int c = 0; c < 8; ++c) {
                 acc[v][c] = acc[v][c] + __shfl_xor(acc[v][c], 16);
@@ -325,14 +356,15 @@ __global__ __launch_bounds__(64) void part_valu_kernel(const PartArgs a) {
             }
     }
 #pragma unroll
-    for (int v = 0; v < NQ; ++v) {
-        if ((v % RPI) != lrow) continue;
+    for (int i = 0; i < VW; ++i) {
+        if ((i % RPI) != lrow) continue;
+        const int v = VW * wave + i;
         const int r = v / G, h = kvh * G + (v % G);
         const size_t slot = (((size_t)(s * R + r) * a.Hq + h) * a.n_splits + split);
         float4 *dst = reinterpret_cast<float4 *>(a.ws_acc + slot * D + lch * 8);
-        dst[0] = make_float4(acc[v][0], acc[v][1], acc[v][2], acc[v][3]);
-        dst[1] = make_float4(acc[v][4], acc[v][5], acc[v][6], acc[v][7]);
-        if (lch == 0) *reinterpret_cast<float2 *>(a.ws_ml + slot * 2) = make_float2(m_run[v], l_tot[v]);
+        dst[0] = make_float4(acc[i][0], acc[i][1], acc[i][2], acc[i][3]);
+        dst[1] = make_float4(acc[i][4], acc[i][5], acc[i][6], acc[i][7]);
+        if (lch == 0) *reinterpret_cast<float2 *>(a.ws_ml + slot * 2) = make_float2(m_run[i], l_tot[i]);
     }
 }
 
@@ -345,11 +377,12 @@ bool valu_supported(int D, int G, int NQ) {
 
 template <int D, int G, int NQ>
 static hipError_t launch_one(const PartArgs &a, int S, hipStream_t st) {
+    constexpr int NW = valu_waves<NQ>();
     const dim3 grid(a.n_splits, a.Hkv, S);
     switch (valu_mode<D>(a.P)) {
-        case 0: hipLaunchKernelGGL((part_valu_kernel<D, G, NQ, 0>), grid, dim3(64), 0, st, a); break;
-        case 1: hipLaunchKernelGGL((part_valu_kernel<D, G, NQ, 1>), grid, dim3(64), 0, st, a); break;
-        default: hipLaunchKernelGGL((part_valu_kernel<D, G, NQ, 2>), grid, dim3(64), 0, st, a); break;
+        case 0: hipLaunchKernelGGL((part_valu_kernel<D, G, NQ, 0>), grid, dim3(64 * NW), 0, st, a); break;
+        case 1: hipLaunchKernelGGL((part_valu_kernel<D, G, NQ, 1>), grid, dim3(64 * NW), 0, st, a); break;
+        default: hipLaunchKernelGGL((part_valu_kernel<D, G, NQ, 2>), grid, dim3(64 * NW), 0, st, a); break;
     }
     return hipGetLastError();
 }
