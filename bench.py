@@ -41,6 +41,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--quick", action="store_true", help="skip the side measurements")
     ap.add_argument("--fixed-length", type=int, default=None, help="all 12 streams at this length")
+    ap.add_argument("--calib-copy", action="store_true", help="also run a 1 GiB device copy (counter calibration)")
     return ap.parse_args()
 
 
@@ -129,6 +130,107 @@ def cold_calls(setup, iters, torch):
         ms.append(a.elapsed_time(b))
     ms.sort()
     return ms[len(ms) // 2]
+
+
+def event_ms(fn, iters, torch, warmup=3):
+    """Mean GPU time of fn() over iters back-to-back calls (HIP events on the current stream)."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(iters):
+        fn()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / iters
+
+
+def attn_flops(lengths, rows, q_heads, head_dim, window=0):
+    """Multiply-adds of QK^T and PV, counted as 2 flops each, over the keys each row sees."""
+    total = 0
+    for L in lengths:
+        for r in range(rows):
+            p = L - rows + r
+            lo = 0 if window <= 0 else max(0, p - window + 1)
+            total += (p + 1 - lo)
+    return 4 * total * q_heads * head_dim
+
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
+def other_workloads(torch, binding, staging, workloads):
+    """The verify window, the wide-head pair and the prompt chunks, timed on their own."""
+    res = {}
+    # speculative verify window: 4 streams x 8 rows x ~9k, GQA 8 (MFMA path)
+    w = workloads.verify_window()
+    c = staging.make_cache(w, order=workloads.free_order(w.pool_pages, 3003))
+    ks, vs = workloads.kv_history(w, device="cuda")
+    staging.write_history(c, ks, vs)
+    q = workloads.queries(w, device="cuda")
+    out = torch.empty_like(q)
+    ws = torch.empty(binding.workspace_size(c.pool, c.table, c.seq_len, w.rows, w.q_heads, c.max_seq_len),
+                     dtype=torch.uint8, device="cuda")
+    ms = event_ms(lambda: binding.verify(c.pool, q, c.table, c.seq_len, c.max_seq_len, out=out, workspace=ws), 50, torch)
+    by = sum(c.lengths) * w.kv_bytes_per_token
+    fl = attn_flops(c.lengths, w.rows, w.q_heads, w.head_dim)
+    res["verify_window_4x8rows_9k"] = {"us": round(ms * 1e3, 2), "kv_GBps": round(by / ms / 1e6, 1),
+                                       "TFLOPs": round(fl / ms / 1e9, 2),
+                                       "mfma_frac": round(fl / ms / 1e9 / MFMA_BF16_PEAK_TFLOPS, 4),
+                                       "kv_bytes": by, "flops": fl}
+    del c, ks, vs
+    # wide head: d 512, pages of 37; stream 0 decodes at 2048, stream 1 verifies 4 rows at 9000
+    w = workloads.wide_head()
+    c = staging.make_cache(w, order=workloads.free_order(w.pool_pages, 3004))
+    ks, vs = workloads.kv_history(w, device="cuda")
+    staging.write_history(c, ks, vs)
+    q0 = workloads.normal_bf16((1, 1, w.q_heads, 512), 4101, "cuda")
+    q1 = workloads.normal_bf16((1, 4, w.q_heads, 512), 4102, "cuda")
+    t0, l0 = c.stream_view(0)
+    t1, l1 = c.stream_view(1)
+    ms0 = event_ms(lambda: binding.decode(c.pool, q0, t0, l0, c.lengths[0]), 50, torch)
+    ms1 = event_ms(lambda: binding.verify(c.pool, q1, t1, l1, c.lengths[1]), 50, torch)
+    b0, b1 = c.lengths[0] * w.kv_bytes_per_token, c.lengths[1] * w.kv_bytes_per_token
+    res["wide_head_d512_p37"] = {"decode_2048_us": round(ms0 * 1e3, 2), "decode_kv_GBps": round(b0 / ms0 / 1e6, 1),
+                                 "verify4_9000_us": round(ms1 * 1e3, 2), "verify_kv_GBps": round(b1 / ms1 / 1e6, 1)}
+    del c, ks, vs
+    # prompt: 2048 tokens in 4 chunks of 512 rows, full layer and sliding layer (window 1024, ring)
+    for window in (0, 1024):
+        w = workloads.prefill_mixed(window=window)
+        c = staging.make_cache(w, order=workloads.free_order(w.pool_pages, 3005), lengths=[2048])
+        ks, vs = workloads.kv_history(w, device="cuda")
+        qa = workloads.normal_bf16((1, 2048, w.q_heads, w.head_dim), 77, "cuda")
+        seqs = [torch.tensor([c0 + 512], dtype=torch.int32, device="cuda") for c0 in range(0, 2048, 512)]
+        kn = [ks[0][c0:c0 + 512][None].contiguous() for c0 in range(0, 2048, 512)]
+        vn = [vs[0][c0:c0 + 512][None].contiguous() for c0 in range(0, 2048, 512)]
+        qs = [qa[:, c0:c0 + 512].contiguous() for c0 in range(0, 2048, 512)]
+
+        def prompt():
+            for i in range(4):
+                binding.rows_put(c.pool, c.table, seqs[i], kn[i], vn[i], 2048, ring_pages=c.ring_pages)
+                binding.prefill(c.pool, qs[i], c.table, seqs[i], 2048, window=window, ring_pages=c.ring_pages)
+        ms = event_ms(prompt, 10, torch)
+        fl = sum(attn_flops([c0 + 512], 512, w.q_heads, w.head_dim, window) for c0 in range(0, 2048, 512))
+        res["prefill_2048_in_512_chunks" + ("_window1024_ring" if window else "_full")] = {
+            "us": round(ms * 1e3, 2), "us_per_chunk": round(ms * 1e3 / 4, 2), "TFLOPs": round(fl / ms / 1e9, 2),
+            "mfma_frac": round(fl / ms / 1e9 / MFMA_BF16_PEAK_TFLOPS, 4), "flops": fl}
+        del c, ks, vs
+    torch.cuda.empty_cache()
+    return res
+
+
+def calibration_copy(torch, nbytes=1 << 30, reps=3):
+    """An elementwise kernel of known traffic (reads nbytes, writes nbytes: bitwise_not over
+    int32), so that profiler byte counters can be scaled against it.  A plain copy_ may go to
+    the DMA engines, which kernel counters do not see."""
+    src = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        torch.bitwise_not(src, out=dst)
+    torch.cuda.synchronize()
+    del src, dst
 
 
 def cpu_baseline(setup, oracle, workloads, budget_s=20.0):
@@ -246,6 +348,13 @@ def main():
                                         "part_kv_GBps": round(fx.kv_bytes / (fpart * 1e-3) / 1e9, 1)}
             del fx
             torch.cuda.empty_cache()
+
+    if not args.quick:
+        log("[bench] verify window, wide head and prompt workloads")
+        result["other_workloads"] = other_workloads(torch, binding, staging, workloads)
+    if args.calib_copy:
+        log("[bench] calibration copy")
+        calibration_copy(torch)
 
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle)")
