@@ -132,19 +132,34 @@ def cold_calls(setup, iters, torch):
     return ms[len(ms) // 2]
 
 
-def event_ms(fn, iters, torch, warmup=3):
-    """Mean GPU time of fn() over iters back-to-back calls (HIP events on the current stream)."""
-    for _ in range(warmup):
+def graph_us(fn, torch, reps=20, iters=5, check=None):
+    """GPU time per fn() call in µs: `reps` calls captured into one HIP graph, replayed `iters`
+    times between two events, so host-side launch cost does not show.  `check` (a tensor fn
+    writes) is compared byte for byte between the eager call and the last replay."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
         fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    eager = check.clone() if check is not None else None
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(reps):
+            fn()
+    g.replay()
     torch.cuda.synchronize()
     a = torch.cuda.Event(enable_timing=True)
     b = torch.cuda.Event(enable_timing=True)
     a.record()
     for _ in range(iters):
-        fn()
+        g.replay()
     b.record()
     torch.cuda.synchronize()
-    return a.elapsed_time(b) / iters
+    if check is not None and not torch.equal(eager.view(torch.int16), check.view(torch.int16)):
+        raise RuntimeError("graph replay differs from the eager call")
+    del g
+    return a.elapsed_time(b) * 1e3 / (iters * reps)
 
 
 def attn_flops(lengths, rows, q_heads, head_dim, window=0):
@@ -162,7 +177,8 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0
 
 
 def other_workloads(torch, binding, staging, workloads):
-    """The verify window, the wide-head pair and the prompt chunks, timed on their own."""
+    """The verify window, the wide-head pair and the prompt chunks, timed on their own as GPU
+    time per call (HIP graph replays, so host launch cost does not show)."""
     res = {}
     # speculative verify window: 4 streams x 8 rows x ~9k, GQA 8 (MFMA path)
     w = workloads.verify_window()
@@ -173,12 +189,14 @@ def other_workloads(torch, binding, staging, workloads):
     out = torch.empty_like(q)
     ws = torch.empty(binding.workspace_size(c.pool, c.table, c.seq_len, w.rows, w.q_heads, c.max_seq_len),
                      dtype=torch.uint8, device="cuda")
-    ms = event_ms(lambda: binding.verify(c.pool, q, c.table, c.seq_len, c.max_seq_len, out=out, workspace=ws), 50, torch)
+    us = graph_us(lambda: binding.verify(c.pool, q, c.table, c.seq_len, c.max_seq_len, out=out, workspace=ws),
+                  torch, check=out)
     by = sum(c.lengths) * w.kv_bytes_per_token
     fl = attn_flops(c.lengths, w.rows, w.q_heads, w.head_dim)
-    res["verify_window_4x8rows_9k"] = {"us": round(ms * 1e3, 2), "kv_GBps": round(by / ms / 1e6, 1),
-                                       "TFLOPs": round(fl / ms / 1e9, 2),
-                                       "mfma_frac": round(fl / ms / 1e9 / MFMA_BF16_PEAK_TFLOPS, 4),
+    res["verify_window_4x8rows_9k"] = {"us": round(us, 2), "kv_GBps": round(by / us / 1e3, 1),
+                                       "hbm_frac": round(by / us / 1e3 / HBM_PEAK_GBS, 4),
+                                       "TFLOPs": round(fl / us / 1e6, 2),
+                                       "mfma_frac": round(fl / us / 1e6 / MFMA_BF16_PEAK_TFLOPS, 4),
                                        "kv_bytes": by, "flops": fl}
     del c, ks, vs
     # wide head: d 512, pages of 37; stream 0 decodes at 2048, stream 1 verifies 4 rows at 9000
@@ -190,11 +208,12 @@ def other_workloads(torch, binding, staging, workloads):
     q1 = workloads.normal_bf16((1, 4, w.q_heads, 512), 4102, "cuda")
     t0, l0 = c.stream_view(0)
     t1, l1 = c.stream_view(1)
-    ms0 = event_ms(lambda: binding.decode(c.pool, q0, t0, l0, c.lengths[0]), 50, torch)
-    ms1 = event_ms(lambda: binding.verify(c.pool, q1, t1, l1, c.lengths[1]), 50, torch)
+    o0, o1 = torch.empty_like(q0), torch.empty_like(q1)
+    us0 = graph_us(lambda: binding.decode(c.pool, q0, t0, l0, c.lengths[0], out=o0), torch, check=o0)
+    us1 = graph_us(lambda: binding.verify(c.pool, q1, t1, l1, c.lengths[1], out=o1), torch, check=o1)
     b0, b1 = c.lengths[0] * w.kv_bytes_per_token, c.lengths[1] * w.kv_bytes_per_token
-    res["wide_head_d512_p37"] = {"decode_2048_us": round(ms0 * 1e3, 2), "decode_kv_GBps": round(b0 / ms0 / 1e6, 1),
-                                 "verify4_9000_us": round(ms1 * 1e3, 2), "verify_kv_GBps": round(b1 / ms1 / 1e6, 1)}
+    res["wide_head_d512_p37"] = {"decode_2048_us": round(us0, 2), "decode_kv_GBps": round(b0 / us0 / 1e3, 1),
+                                 "verify4_9000_us": round(us1, 2), "verify_kv_GBps": round(b1 / us1 / 1e3, 1)}
     del c, ks, vs
     # prompt: 2048 tokens in 4 chunks of 512 rows, full layer and sliding layer (window 1024, ring)
     for window in (0, 1024):
@@ -207,15 +226,18 @@ def other_workloads(torch, binding, staging, workloads):
         vn = [vs[0][c0:c0 + 512][None].contiguous() for c0 in range(0, 2048, 512)]
         qs = [qa[:, c0:c0 + 512].contiguous() for c0 in range(0, 2048, 512)]
 
+        outs = [torch.empty_like(x) for x in qs]
+
         def prompt():
             for i in range(4):
                 binding.rows_put(c.pool, c.table, seqs[i], kn[i], vn[i], 2048, ring_pages=c.ring_pages)
-                binding.prefill(c.pool, qs[i], c.table, seqs[i], 2048, window=window, ring_pages=c.ring_pages)
-        ms = event_ms(prompt, 10, torch)
+                binding.prefill(c.pool, qs[i], c.table, seqs[i], 2048, window=window, ring_pages=c.ring_pages,
+                                out=outs[i])
+        us = graph_us(prompt, torch, reps=5, check=outs[3])
         fl = sum(attn_flops([c0 + 512], 512, w.q_heads, w.head_dim, window) for c0 in range(0, 2048, 512))
         res["prefill_2048_in_512_chunks" + ("_window1024_ring" if window else "_full")] = {
-            "us": round(ms * 1e3, 2), "us_per_chunk": round(ms * 1e3 / 4, 2), "TFLOPs": round(fl / ms / 1e9, 2),
-            "mfma_frac": round(fl / ms / 1e9 / MFMA_BF16_PEAK_TFLOPS, 4), "flops": fl}
+            "us": round(us, 2), "us_per_chunk": round(us / 4, 2), "TFLOPs": round(fl / us / 1e6, 2),
+            "mfma_frac": round(fl / us / 1e6 / MFMA_BF16_PEAK_TFLOPS, 4), "flops": fl}
         del c, ks, vs
     torch.cuda.empty_cache()
     return res

@@ -28,6 +28,14 @@ FLAGS = [
 ]
 
 
+# Per-source flags.  The MFMA kernels keep their accumulators in ordinary VGPRs (gfx950 MFMA
+# reads and writes them directly); with AGPR accumulators the softmax and the rescale of the
+# output move every value through v_accvgpr_read/write.
+SOURCE_FLAGS = {
+    "kernels_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
+
+
 def hipcc() -> str:
     for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
         if cand and os.path.exists(cand):
@@ -40,6 +48,7 @@ def _compile(src: str, verbose: bool):
     cmd = [hipcc(), *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
     if src.endswith(".hip"):
         cmd += ["-x", "hip", "-Rpass-analysis=kernel-resource-usage"]
+    cmd += SOURCE_FLAGS.get(src, [])
     if verbose:
         print(" ".join(cmd), flush=True)
     p = subprocess.run(cmd, capture_output=True, text=True)

@@ -104,7 +104,8 @@ kv_status deep_check(const kv_pool *pool, const kv_layout *lay, int64_t ring_spa
 
 struct Plan {
     bool mfma;
-    int D, G, Hkv, Hq, S, R, chunk, n_splits, tiles;
+    int D, G, Hkv, Hq, S, R, chunk, n_splits;
+    kvp::MfmaPlan mp;
 };
 
 int splits_for(int max_seq_len, int rows, int window, int chunk) {
@@ -141,13 +142,12 @@ kv_status make_plan(const kv_pool *pool, const kv_layout *lay, const kv_attn_arg
     if (p->mfma) {
         if (!kvp::mfma_supported(p->D, p->G, p->R))
             return fail(KV_E_SHAPE, "%s: no MFMA kernel for head_dim %d, group %d, rows %d", who, p->D, p->G, p->R);
-        p->chunk = kvp::mfma_chunk(p->D);
-        p->tiles = kvp::mfma_query_tiles(p->D, p->G, p->R);
+        p->mp = kvp::mfma_plan(p->D, p->G, p->R, p->S, p->Hkv, lay->max_seq_len, a->window);
+        p->chunk = p->mp.chunk;
     } else {
         if (!kvp::valu_supported(p->D, p->G, nq))
             return fail(KV_E_SHAPE, "%s: no VALU kernel for head_dim %d, group %d, rows %d", who, p->D, p->G, p->R);
         p->chunk = kvp::valu_chunk(p->D);
-        p->tiles = 1;
     }
     p->n_splits = splits_for(lay->max_seq_len, p->R, a->window, p->chunk);
     return ok();
@@ -189,12 +189,13 @@ kv_status run_attention(const kv_pool *pool, const kv_layout *lay, const kv_attn
     pa.Hq = p.Hq;
     pa.window = a->window;
     pa.n_splits = p.n_splits;
+    pa.chunk = p.chunk;
     const float scale = a->scale > 0.f ? a->scale : 1.0f / std::sqrt((float)p.D);
     pa.scale_log2 = scale * 1.4426950408889634f;
 
     if (g_part_start && hipEventRecord(g_part_start, hs) != hipSuccess)
         return fail(KV_E_DEVICE, "%s: recording the start event failed", who);
-    hipError_t e = p.mfma ? kvp::launch_part_mfma(p.D, p.G, pa, p.S, hs)
+    hipError_t e = p.mfma ? kvp::launch_part_mfma(p.D, p.G, p.mp, pa, p.S, hs)
                           : kvp::launch_part_valu(p.D, p.G, p.R * p.G, pa, p.S, hs);
     if (e != hipSuccess) return fail(KV_E_DEVICE, "%s: part kernel launch failed: %s", who, hipGetErrorString(e));
     if (g_part_stop && hipEventRecord(g_part_stop, hs) != hipSuccess)

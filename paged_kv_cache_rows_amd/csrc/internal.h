@@ -32,6 +32,9 @@ struct PartArgs {
     float *ws_ml;    // [S][R][Hq][n_splits][2]
     int num_pages, P, Hkv, stride, ring_pages;
     int R, Hq, window, n_splits;
+    int chunk;         // keys per split (a multiple of the kernel's key tile)
+    int S, tiles;      // streams and query tiles per (stream, KV head) of an MFMA call
+    int per_xcd;       // MFMA work items per XCD (the grid is 8 * per_xcd workgroups)
     float scale_log2;  // scale * log2(e)
 };
 
@@ -46,14 +49,20 @@ struct MergeArgs {
 // Keys per split (workgroup) of each path; split boundaries are multiples of this in absolute
 // positions, so they depend on (L, R, W, D) only and never on physical page ids.
 int valu_chunk(int D);
-int mfma_chunk(int D);
 bool valu_supported(int D, int G, int NQ);
 bool mfma_supported(int D, int G, int R);
-int mfma_query_tiles(int D, int G, int R);  // query tiles per (stream, KV head)
+
+// Launch shape of the MFMA part kernel for one call: query-column blocks per wave (tile of
+// 64 * qw query vectors), query tiles per (stream, KV head), keys per split.  A function of
+// the call's shape only.
+struct MfmaPlan {
+    int qw, tiles, chunk;
+};
+MfmaPlan mfma_plan(int D, int G, int R, int S, int Hkv, int max_seq_len, int window);
 
 hipError_t launch_rows_put(const RowsArgs &a, hipStream_t st);
 hipError_t launch_part_valu(int D, int G, int NQ, const PartArgs &a, int S, hipStream_t st);
-hipError_t launch_part_mfma(int D, int G, const PartArgs &a, int S, hipStream_t st);
+hipError_t launch_part_mfma(int D, int G, const MfmaPlan &p, const PartArgs &a, int S, hipStream_t st);
 hipError_t launch_merge(const MergeArgs &a, hipStream_t st);
 
 }  // namespace kvp

@@ -4,16 +4,24 @@
 // TensorFold PR #1620, opening description (Reads bullet: prompts and drafted verify read keys
 // through the page table) and TensorFold PR #2730 (verify windows of up to eight rows).
 //
-// Design for gfx950.  A workgroup of 4 waves takes a tile of 64 query vectors of one KV head
-// (rows x GQA heads, row-major) and one chunk of keys; each wave owns 16 query vectors.
-//  * K and V tiles of KT keys are loaded cooperatively through the page table (entries of the
-//    chunk cached in LDS) into LDS; K row-major, V transposed (keys contiguous per channel).
+// Design for gfx950.  A workgroup of 4 waves takes a tile of 64 * QW query vectors of one KV
+// head (rows x GQA heads, row-major) and one chunk of keys; each wave owns QW blocks of 16
+// query vectors.
+//  * K and V tiles of KT keys are loaded through the page table (one lookup per tile when the
+//    page size is a multiple of KT, else per 16-byte piece from a copy of the chunk's table
+//    entries in LDS) into registers, one tile ahead, then staged in LDS: K row-major, V
+//    transposed into 8-byte units of 4 keys of one channel.  Each thread loads 4 (or 8)
+//    consecutive keys of one 8-channel block, so the transpose is a register permute and the
+//    unit stores are 8 bytes wide; the units are XOR-swizzled so that both the stores and the
+//    MFMA operand reads touch every LDS bank equally.
 //  * Scores are computed transposed, S^T = K Q^T, with v_mfma_f32_16x16x32_bf16: the wave's
-//    queries are the B operand, held in registers for the whole chunk.  In the C layout a lane
-//    owns one query column and 4 keys per 16-key block, which is exactly the B-operand layout
-//    that O^T = V^T P^T needs, so the softmax weights feed the second MFMA from registers.
+//    queries are the B operand, held in registers for the whole chunk, and each K fragment read
+//    from LDS feeds QW MFMAs.  In the C layout a lane owns one query column and 4 keys per
+//    16-key block, which is exactly the B-operand layout that O^T = V^T P^T needs, so the
+//    softmax weights feed the second MFMA from registers.
 //  * Online softmax per query column in the log2 domain; masked keys are selected out and V
-//    rows outside the chunk are zeroed, so NaN in unused slots never reaches the sums.
+//    units outside the chunk are zeroed, so NaN in unused slots never reaches the sums.  Tiles
+//    that every column sees in full skip the mask.
 //  * The workgroup writes an unnormalised partial (acc, m, l) per query vector, merged later
 //    in fixed chunk order.
 #include "internal.h"
@@ -27,56 +35,99 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 template <int D>
 struct MfmaGeom {
     static constexpr int KT = D == 128 ? 64 : 32;       // keys per tile
-    static constexpr int CHUNK = D == 128 ? 256 : 128;  // keys per workgroup
-    static constexpr int KRS = D + 8;                   // K tile row stride (bf16)
-    static constexpr int VRS = KT + 4;                  // V^T row stride (bf16)
-    static constexpr int M = 64;                        // query vectors per workgroup
+    static constexpr int KRS = D + 16;                  // K tile row stride (bf16): 288 or 1056 bytes, so
+                                                        // that an MFMA operand read is free of bank conflicts
+    static constexpr int CB = D / 8;                    // 16-byte channel blocks per row
     static constexpr int NT = 256;                      // threads
-    static constexpr int LC = KT * D / 8 / NT;          // 16-byte pieces per thread per operand
-    static constexpr int TC = 72;                       // cached page-table entries
+    static constexpr int KPT = KT * CB / NT;            // keys per thread per tile (4 or 8)
+    static constexpr int UPR = KT / 4;                  // V^T units (4 keys) per channel
+    static constexpr int RPS = 32 / UPR;                // channels per 32-unit (256-byte) row
+    static constexpr int TC = 160;                      // cached page-table entries
 };
 
-int mfma_chunk(int D) { return D == 512 ? MfmaGeom<512>::CHUNK : MfmaGeom<128>::CHUNK; }
+static_assert(MfmaGeom<128>::KPT == 4 && MfmaGeom<512>::KPT == 8, "thread tiling");
+
+// Position of the V^T unit (channel ch, keys 4 kg .. 4 kg + 3) in units of 8 bytes.  The
+// 32 units of a 256-byte row are permuted by an XOR of the row number's bits, chosen so that
+// a unit store (lanes: 16 or 64 channel blocks x key groups) and an MFMA A-operand read
+// (lanes: 16 channels x 4 key groups) each hit every bank pair exactly twice.
+__host__ __device__ constexpr int vt_swz(int sr) { return (((sr ^ (sr >> 3)) & 7) << 2) ^ ((sr >> 1) & 3); }
+
+template <int D>
+__device__ __forceinline__ int vt_unit(int ch, int kg) {
+    using Geo = MfmaGeom<D>;
+    const int sr = ch / Geo::RPS, rr = ch % Geo::RPS;
+    return sr * 32 + ((rr * Geo::UPR + kg) ^ vt_swz(sr));
+}
+
+int mfma_tile_keys(int D) { return D == 512 ? MfmaGeom<512>::KT : MfmaGeom<128>::KT; }
 
 bool mfma_supported(int D, int G, int R) {
     return (D == 128 || D == 512) && (G == 4 || G == 8) && R >= 1 && R * G >= 16;
 }
 
-int mfma_query_tiles(int D, int G, int R) {
-    (void)D;
-    return (R * G + 63) / 64;
-}
-
-template <int D>
-static bool mfma_cached(int P) {
-    using Geo = MfmaGeom<D>;
-    return (Geo::CHUNK + Geo::KT) / P + 2 <= Geo::TC;
+// Query-column blocks per wave, query tiles and chunk length of one call.  Everything here is
+// a function of the call's shape (never of page ids or device lengths), so the chunk
+// boundaries, and with them the result, do not depend on where pages live.
+MfmaPlan mfma_plan(int D, int G, int R, int S, int Hkv, int max_seq_len, int window) {
+    MfmaPlan p;
+    const int nq = R * G;
+    // one 16-column block per wave: two (QW = 2) halve the LDS reads per MFMA but need
+    // about 280 registers, one wave per SIMD, and measured slower on every workload here
+    p.qw = 1;
+    p.tiles = (nq + 64 * p.qw - 1) / (64 * p.qw);
+    const int kt = mfma_tile_keys(D);
+    int span = max_seq_len;
+    if (window > 0 && (int64_t)window + R - 1 < span) span = window + R - 1;
+    if (span < 1) span = 1;
+    const int64_t groups = (int64_t)S * Hkv * p.tiles;
+    // aim at 2 (verify windows, bound by HBM) or 4 (prompt chunks, whose causal triangle
+    // leaves part of the grid idle) workgroups per CU over the whole call: long enough chunks
+    // to amortise the per-workgroup set-up, short enough to keep every CU busy
+    const int64_t target = nq >= 256 ? 1024 : 512;
+    int64_t chunk = ((int64_t)span * groups + target - 1) / target;
+    chunk = (chunk + kt - 1) / kt * kt;
+    const int lo = 4 * kt, hi = 64 * kt;
+    if (chunk < lo) chunk = lo;
+    if (chunk > hi) chunk = hi;
+    p.chunk = (int)chunk;
+    return p;
 }
 
 __device__ __forceinline__ f32x4_t mfma16(const bf16x8_t &a, const bf16x8_t &b, const f32x4_t &c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-template <int D, int G, bool CACHED>
+// MODE 0: P % KT == 0 and the chunk's table entries cached in LDS (one lookup per tile);
+// MODE 1: entries cached, lookup per piece; MODE 2: lookup per piece in the global table.
+template <int D, int G, int QW, int MODE>
 __global__ __launch_bounds__(256) void part_mfma_kernel(const PartArgs a) {
     using Geo = MfmaGeom<D>;
-    constexpr int KT = Geo::KT, CHUNK = Geo::CHUNK, KRS = Geo::KRS, VRS = Geo::VRS, M = Geo::M;
-    constexpr int LC = Geo::LC, TC = Geo::TC;
+    constexpr int KT = Geo::KT, KRS = Geo::KRS, CB = Geo::CB, KPT = Geo::KPT, TC = Geo::TC;
+    constexpr int M = 64 * QW;       // query vectors per workgroup
     constexpr int NB = KT / 16;      // 16-key blocks per tile
     constexpr int NKB = D / 32;      // 32-channel blocks (QK k-steps)
     constexpr int NCB = D / 16;      // 16-channel blocks (PV output blocks)
     constexpr int NPM = KT / 32;     // 32-key PV k-steps
 
     __shared__ __attribute__((aligned(16))) uint16_t k_lds[KT * KRS];
-    __shared__ __attribute__((aligned(16))) uint16_t vt_lds[D * VRS];
+    __shared__ __attribute__((aligned(16))) uint2 vt_lds[D * KT / 4];
     __shared__ int32_t t_lds[TC];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int col = lane & 15, grp = lane >> 4;
-    const int split = blockIdx.x, s = blockIdx.z;
-    const int kvh = blockIdx.y % a.Hkv, tile = blockIdx.y / a.Hkv;
-    const int R = a.R, W = a.window;
+    // work item: the dispatcher hands workgroups to the 8 XCDs round-robin (dispatch id
+    // d goes to XCD d mod 8), so XCD x gets the contiguous items [x per, (x + 1) per), ordered
+    // (stream, KV head, split, tile) with the tile fastest: the query tiles that share a key
+    // chunk run together on one XCD and reread it from that XCD's L2, not from HBM
+    const int item = (blockIdx.x & 7) * a.per_xcd + (blockIdx.x >> 3);
+    if (item >= a.S * a.Hkv * a.n_splits * a.tiles) return;
+    const int tile = item % a.tiles;
+    const int split = (item / a.tiles) % a.n_splits;
+    const int kvh = (item / (a.tiles * a.n_splits)) % a.Hkv;
+    const int s = item / (a.tiles * a.n_splits * a.Hkv);
+    const int R = a.R, W = a.window, CH = a.chunk;
     const int L = a.seq_len[s];
     const int NQ = R * G;
     const int v0 = tile * M;
@@ -85,29 +136,33 @@ __global__ __launch_bounds__(256) void part_mfma_kernel(const PartArgs a) {
     const int r_last = (min(NQ, v0 + M) - 1) / G;
     const int p_first = L - R + r_first, p_last = L - R + r_last;
     const int lo_stream = W > 0 ? max(0, L - R - W + 1) : 0;
-    const int c0 = (lo_stream / CHUNK + split) * CHUNK;
+    const int c0 = (lo_stream / CH + split) * CH;
     const int lo_tile = W > 0 ? max(0, p_first - W + 1) : 0;
     const int kbeg = max(c0, lo_tile);
-    const int kend = min(c0 + CHUNK, p_last + 1);
+    const int kend = min(c0 + CH, p_last + 1);
     if (kbeg >= kend) return;        // no row of the tile sees this chunk: nothing to merge
+    const int lo_full = W > 0 ? p_last - W + 1 : 0;   // every column sees keys >= this ...
+    const int hi_full = p_first;                      // ... and <= this
 
-    // this lane's query column
-    const int vq = v0 + wave * 16 + col;
-    const bool col_ok = vq < NQ;
-    const int rq = col_ok ? vq / G : 0;
-    const int hq = kvh * G + (col_ok ? vq % G : 0);
-    const int p_col = L - R + rq;
-    const int lo_col = W > 0 ? p_col - W + 1 : 0;
-
-    // queries as the B operand of S^T = K Q^T: lane holds channels 32 kb + 8 grp .. + 8
-    bf16x8_t qf[NKB];
-    {
-        const uint16_t *qrow = a.q + ((size_t)(s * R + rq) * a.Hq + hq) * D + 8 * grp;
+    // this lane's query columns, and the queries as the B operand of S^T = K Q^T: the lane
+    // holds channels 32 kb + 8 grp .. + 8 of its column
+    bool col_ok[QW];
+    int rq[QW], hq[QW], p_col[QW], lo_col[QW];
+    bf16x8_t qf[QW][NKB];
+#pragma unroll
+    for (int b = 0; b < QW; ++b) {
+        const int vq = v0 + (wave * QW + b) * 16 + col;
+        col_ok[b] = vq < NQ;
+        rq[b] = col_ok[b] ? vq / G : 0;
+        hq[b] = kvh * G + (col_ok[b] ? vq % G : 0);
+        p_col[b] = L - R + rq[b];
+        lo_col[b] = W > 0 ? p_col[b] - W + 1 : 0;
+        const uint16_t *qrow = a.q + ((size_t)(s * R + rq[b]) * a.Hq + hq[b]) * D + 8 * grp;
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) {
             u32x4 x = *reinterpret_cast<const u32x4 *>(qrow + 32 * kb);
-            if (!col_ok) x = u32x4{0, 0, 0, 0};
-            qf[kb] = __builtin_bit_cast(bf16x8_t, x);
+            if (!col_ok[b]) x = u32x4{0, 0, 0, 0};
+            qf[b][kb] = __builtin_bit_cast(bf16x8_t, x);
         }
     }
 
@@ -116,7 +171,7 @@ __global__ __launch_bounds__(256) void part_mfma_kernel(const PartArgs a) {
     const int nt = (kend - kt_first + KT - 1) / KT;
     const int idx0 = kt_first / P;
     const int32_t *trow = a.table + (size_t)s * a.stride;
-    if (CACHED) {
+    if (MODE != 2) {
         for (int i = tid; i < TC; i += Geo::NT) {
             int idx = idx0 + i;
             if (a.ring_pages) idx %= a.ring_pages;
@@ -129,148 +184,248 @@ __global__ __launch_bounds__(256) void part_mfma_kernel(const PartArgs a) {
 
     const size_t page_elems = (size_t)a.Hkv * P * D;
     const size_t head_off = (size_t)kvh * P * D;
-    // piece u of this thread: key row kr[u] of the tile, channels 8 * kc[u] .. + 8
-    u32x4 kreg[LC], vreg[LC];
-    auto load_tile = [&](int tb, u32x4 (&kq)[LC], u32x4 (&vq_)[LC]) {
+    // this thread's pieces: keys KPT kq .. KPT kq + KPT - 1 of a tile, channels 8 kc .. + 8
+    const int kc = tid % CB, kq = tid / CB;
+    u32x4 kreg0[KPT], vreg0[KPT], kreg1[KPT], vreg1[KPT];
+    auto load_tile = [&](int tb, u32x4 (&kreg)[KPT], u32x4 (&vreg)[KPT]) {
+        if (MODE == 0) {
+            // the whole tile lies in one page
+            const int idx = tb / P;
+            const int pg = max(t_lds[idx - idx0], 0);
+            const size_t base = (size_t)pg * page_elems + head_off + (size_t)(tb - idx * P + KPT * kq) * D + 8 * kc;
 #pragma unroll
-        for (int u = 0; u < LC; ++u) {
-            const int c = tid + Geo::NT * u;
-            const int kr = c / (D / 8), kc = c % (D / 8);
-            const int j = tb + kr;
-            int idx = j / P;
-            const int off = j - idx * P;
-            int pg;
-            if (CACHED) {
-                pg = t_lds[idx - idx0];
-            } else {
-                if (a.ring_pages) idx %= a.ring_pages;
-                const int tp = trow[min(idx, a.stride - 1)];
-                pg = (idx < a.stride && (unsigned)tp < (unsigned)a.num_pages) ? tp : -1;
+            for (int u = 0; u < KPT; ++u) {
+                kreg[u] = *reinterpret_cast<const u32x4 *>(a.k_pages + base + (size_t)u * D);
+                vreg[u] = *reinterpret_cast<const u32x4 *>(a.v_pages + base + (size_t)u * D);
             }
-            const size_t e = (size_t)max(pg, 0) * page_elems + head_off + (size_t)off * D + 8 * kc;
-            kq[u] = *reinterpret_cast<const u32x4 *>(a.k_pages + e);
-            vq_[u] = *reinterpret_cast<const u32x4 *>(a.v_pages + e);
+        } else {
+#pragma unroll
+            for (int u = 0; u < KPT; ++u) {
+                const int j = tb + KPT * kq + u;
+                int idx = j / P;
+                const int off = j - idx * P;
+                int pg;
+                if (MODE == 1) {
+                    pg = t_lds[idx - idx0];
+                } else {
+                    if (a.ring_pages) idx %= a.ring_pages;
+                    const int tp = trow[min(idx, a.stride - 1)];
+                    pg = (idx < a.stride && (unsigned)tp < (unsigned)a.num_pages) ? tp : -1;
+                }
+                const size_t e = (size_t)max(pg, 0) * page_elems + head_off + (size_t)off * D + 8 * kc;
+                kreg[u] = *reinterpret_cast<const u32x4 *>(a.k_pages + e);
+                vreg[u] = *reinterpret_cast<const u32x4 *>(a.v_pages + e);
+            }
         }
     };
 
-    f32x4_t o[NCB];
+    f32x4_t o[QW][NCB];
+    float m_run[QW], l_run[QW];
 #pragma unroll
-    for (int cb = 0; cb < NCB; ++cb) o[cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    float m_run = -INFINITY, l_run = 0.f;
-    const float scale_log2 = a.scale_log2;
+    for (int b = 0; b < QW; ++b) {
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) o[b][cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        m_run[b] = -INFINITY;
+        l_run[b] = 0.f;
+    }
+    const float c2 = a.scale_log2;
 
-    load_tile(kt_first, kreg, vreg);
-    for (int it = 0; it < nt; ++it) {
+    // V^T operand reads (channel 16 cb + col, unit 8 pm + 4 hh + grp): vt_swz is linear over
+    // GF(2) and the row number 16 cb / RPS + col / RPS has disjoint bit fields, so the unit
+    // index is (lane part ^ instruction constant) + lane row + instruction row
+    constexpr int RPS = Geo::RPS, CPS = 16 / RPS;
+    const int vt_row_l = (col / RPS) * 32;
+    const int vt_x_l = ((col % RPS) * Geo::UPR + grp) ^ vt_swz(col / RPS);
+
+    // NPF tiles in flight (2 at d 128; 1 at d 512, where a tile is 8 registers x 4 per
+    // thread and operand): tile it + NPF is loaded into the registers that tile it was staged
+    // from; loads past the last tile reread it (in bounds, never staged), and with NPF = 2 an
+    // odd tile count is padded with one tile whose keys are all masked out
+    constexpr int NPF = D == 128 ? 2 : 1;
+    const int kt_last = kt_first + (nt - 1) * KT;
+    auto step = [&](int it, u32x4 (&kreg)[KPT], u32x4 (&vreg)[KPT]) {
         const int tb = kt_first + it * KT;
         lds_fence();
+        // stage: K rows as loaded; V transposed into 4-key units, keys outside [kbeg, kend)
+        // zeroed (they may be unused slots holding NaN)
 #pragma unroll
-        for (int u = 0; u < LC; ++u) {
-            const int c = tid + Geo::NT * u;
-            const int kr = c / (D / 8), kc = c % (D / 8);
-            const int j = tb + kr;
-            *reinterpret_cast<u32x4 *>(k_lds + kr * KRS + 8 * kc) = kreg[u];
-            const uint32_t keep = (j >= kbeg && j < kend) ? 0xFFFFFFFFu : 0u;
-            const u32x4 x = vreg[u] & keep;
-            const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+        for (int u = 0; u < KPT; ++u)
+            *reinterpret_cast<u32x4 *>(k_lds + (KPT * kq + u) * KRS + 8 * kc) = kreg[u];
+        const bool inside = tb >= kbeg && tb + KT <= kend;
+#pragma unroll
+        for (int h = 0; h < KPT / 4; ++h) {
+            u32x4 x[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                x[u] = vreg[4 * h + u];
+                if (!inside) {
+                    const int j = tb + KPT * kq + 4 * h + u;
+                    const uint32_t keep = (j >= kbeg && j < kend) ? 0xFFFFFFFFu : 0u;
+                    x[u] = x[u] & keep;
+                }
+            }
+            const int kg = (KPT * kq) / 4 + h;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                vt_lds[(8 * kc + 2 * i) * VRS + kr] = (uint16_t)(w[i] & 0xFFFFu);
-                vt_lds[(8 * kc + 2 * i + 1) * VRS + kr] = (uint16_t)(w[i] >> 16);
+                const uint2 ev = make_uint2(__builtin_amdgcn_perm(x[1][i], x[0][i], 0x05040100u),
+                                            __builtin_amdgcn_perm(x[3][i], x[2][i], 0x05040100u));
+                const uint2 od = make_uint2(__builtin_amdgcn_perm(x[1][i], x[0][i], 0x07060302u),
+                                            __builtin_amdgcn_perm(x[3][i], x[2][i], 0x07060302u));
+                vt_lds[vt_unit<D>(8 * kc + 2 * i, kg)] = ev;
+                vt_lds[vt_unit<D>(8 * kc + 2 * i + 1, kg)] = od;
             }
         }
-        if (it + 1 < nt) load_tile(tb + KT, kreg, vreg);
+        load_tile(min(tb + NPF * KT, kt_last), kreg, vreg);
         lds_fence();
 
-        // S^T for this wave's 16 query columns
-        f32x4_t sacc[NB];
+        // S^T for this wave's query columns; each K fragment feeds QW MFMAs
+        f32x4_t sacc[QW][NB];
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
-            sacc[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int b = 0; b < QW; ++b) sacc[b][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb) {
                 const bf16x8_t kf = *reinterpret_cast<const bf16x8_t *>(k_lds + (16 * nb + col) * KRS + 32 * kb + 8 * grp);
-                sacc[nb] = mfma16(kf, qf[kb], sacc[nb]);
+#pragma unroll
+                for (int b = 0; b < QW; ++b) sacc[b][nb] = mfma16(kf, qf[b][kb], sacc[b][nb]);
             }
         }
-        // mask, tile max, new running max
-        float tmax = -INFINITY;
+        const bool full = tb >= kbeg && tb + KT <= kend && tb + KT - 1 <= hi_full && tb >= lo_full;
+        bf16x8_t pf[QW][NPM];
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
+        for (int b = 0; b < QW; ++b) {
+            // mask (raw scores; the scale is applied inside the exponent), tile max
+            float tmax = -INFINITY;
+            if (full) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int j = tb + 16 * nb + 4 * grp + r;
-                const bool vis = col_ok && j >= kbeg && j < kend && j <= p_col && j >= lo_col;
-                const float x = vis ? sacc[nb][r] * scale_log2 : -INFINITY;
-                sacc[nb][r] = x;
-                tmax = fmaxf(tmax, x);
+                for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) tmax = fmaxf(tmax, sacc[b][nb][r]);
+            } else {
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int j = tb + 16 * nb + 4 * grp + r;
+                        const bool vis = col_ok[b] && j >= kbeg && j < kend && j <= p_col[b] && j >= lo_col[b];
+                        const float x = vis ? sacc[b][nb][r] : -INFINITY;
+                        sacc[b][nb][r] = x;
+                        tmax = fmaxf(tmax, x);
+                    }
             }
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-        const float m_new = fmaxf(m_run, tmax);
-        const float alpha = (m_new == -INFINITY) ? 1.f : fast_exp2(m_run - m_new);
-        m_run = m_new;
-        float psum = 0.f;
-        bf16x8_t pf[NPM];
+            // the running max of a column moves only when one of its scores exceeds it (rare
+            // after the first tiles): only then is the tile max reduced over the column's four
+            // lane groups and the sums rescaled
+            if (__builtin_amdgcn_ballot_w64(tmax > m_run[b])) {
+                tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+                tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+                const float m_new = fmaxf(m_run[b], tmax);
+                const float mc_new = (m_new == -INFINITY) ? 0.f : m_new * c2;
+                const float alpha = fast_exp2(m_run[b] * c2 - mc_new);   // 0 while nothing was seen
+                m_run[b] = m_new;
+                l_run[b] *= alpha;
+                if (alpha != 1.f) {
 #pragma unroll
-        for (int pm = 0; pm < NPM; ++pm) {
-#pragma unroll
-            for (int h = 0; h < 2; ++h)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const float x = sacc[2 * pm + h][r];
-                    const float p = (x == -INFINITY) ? 0.f : fast_exp2(x - m_new);
-                    psum += p;
-                    pf[pm][4 * h + r] = (__bf16)p;
+                    for (int cb = 0; cb < NCB; ++cb) o[b][cb] *= alpha;
                 }
-        }
-        l_run = l_run * alpha + psum;
-        if (alpha != 1.f) {
+            }
+            const float mc = (m_run[b] == -INFINITY) ? 0.f : m_run[b] * c2;
+            float psum = 0.f;
 #pragma unroll
-            for (int cb = 0; cb < NCB; ++cb) o[cb] *= alpha;
+            for (int pm = 0; pm < NPM; ++pm) {
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const float p = fast_exp2(__builtin_fmaf(sacc[b][2 * pm + hh][r], c2, -mc));
+                        psum += p;
+                        pf[b][pm][4 * hh + r] = (__bf16)p;
+                    }
+            }
+            l_run[b] += psum;
         }
-        // O^T += V^T P^T: A = V^T rows (channels), keys 32 pm + 4 grp + {0..3} and + 16
+        // O^T += V^T P^T: A = V^T rows (channels 16 cb + col), keys 32 pm + 4 grp + {0..3}
+        // and 32 pm + 16 + 4 grp + {0..3}; each V fragment feeds QW MFMAs
+        // (kept opaque so that the 2 NCB NPM addresses are formed in the loop, one ALU op
+        // each, not held in registers across it)
+        int vx = vt_x_l;
+        asm volatile("" : "+v"(vx));
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb) {
 #pragma unroll
             for (int pm = 0; pm < NPM; ++pm) {
-                const uint16_t *vrow = vt_lds + (16 * cb + col) * VRS + 32 * pm + 4 * grp;
-                const uint2 lo = *reinterpret_cast<const uint2 *>(vrow);
-                const uint2 hi = *reinterpret_cast<const uint2 *>(vrow + 16);
-                const u32x4 vv = u32x4{lo.x, lo.y, hi.x, hi.y};
-                o[cb] = mfma16(__builtin_bit_cast(bf16x8_t, vv), pf[pm], o[cb]);
+                const int rowc = CPS * cb * 32;
+                const uint2 lo = vt_lds[((vx ^ ((8 * pm) ^ vt_swz(CPS * cb))) + vt_row_l) + rowc];
+                const uint2 hi = vt_lds[((vx ^ ((8 * pm + 4) ^ vt_swz(CPS * cb))) + vt_row_l) + rowc];
+                const bf16x8_t vv = __builtin_bit_cast(bf16x8_t, u32x4{lo.x, lo.y, hi.x, hi.y});
+#pragma unroll
+                for (int b = 0; b < QW; ++b) o[b][cb] = mfma16(vv, pf[b][pm], o[b][cb]);
             }
         }
+    };
+    load_tile(kt_first, kreg0, vreg0);
+    if (NPF == 2) {
+        // keep the two first tiles in issue order: the wait counts at the top of the loop
+        // assume buffer 0's loads are older than buffer 1's on every path into it
+        asm volatile("" ::: "memory");
+        load_tile(min(kt_first + KT, kt_last), kreg1, vreg1);
+        for (int it = 0; it < nt; it += 2) {
+            step(it, kreg0, vreg0);
+            step(it + 1, kreg1, vreg1);
+        }
+    } else {
+        for (int it = 0; it < nt; ++it) step(it, kreg0, vreg0);
     }
 
     // combine the four key groups' partial sums of each column, write the partials
-    float l_tot = l_run + __shfl_xor(l_run, 16);
-    l_tot = l_tot + __shfl_xor(l_tot, 32);
-    if (col_ok) {
-        const int h = hq;
-        const size_t slot = ((size_t)(s * R + rq) * a.Hq + h) * a.n_splits + split;
-        float *dst = a.ws_acc + slot * D + 4 * grp;
 #pragma unroll
-        for (int cb = 0; cb < NCB; ++cb)
-            *reinterpret_cast<float4 *>(dst + 16 * cb) = make_float4(o[cb][0], o[cb][1], o[cb][2], o[cb][3]);
-        if (grp == 0) *reinterpret_cast<float2 *>(a.ws_ml + slot * 2) = make_float2(m_run, l_tot);
+    for (int b = 0; b < QW; ++b) {
+        float l_tot = l_run[b] + __shfl_xor(l_run[b], 16);
+        l_tot = l_tot + __shfl_xor(l_tot, 32);
+        if (col_ok[b]) {
+            const size_t slot = ((size_t)(s * R + rq[b]) * a.Hq + hq[b]) * a.n_splits + split;
+            float *dst = a.ws_acc + slot * D + 4 * grp;
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb)
+                *reinterpret_cast<float4 *>(dst + 16 * cb) =
+                    make_float4(o[b][cb][0], o[b][cb][1], o[b][cb][2], o[b][cb][3]);
+            if (grp == 0) {
+                const float m2 = m_run[b] == -INFINITY ? -INFINITY : m_run[b] * c2;
+                *reinterpret_cast<float2 *>(a.ws_ml + slot * 2) = make_float2(m2, l_tot);
+            }
+        }
     }
 }
 
-template <int D, int G>
-static hipError_t launch_d_g(const PartArgs &a, int S, hipStream_t st) {
-    const dim3 grid(a.n_splits, a.Hkv * mfma_query_tiles(D, G, a.R), S);
-    if (mfma_cached<D>(a.P))
-        hipLaunchKernelGGL((part_mfma_kernel<D, G, true>), grid, dim3(256), 0, st, a);
+template <int D, int G, int QW>
+static hipError_t launch_dgq(const PartArgs &a, hipStream_t st) {
+    using Geo = MfmaGeom<D>;
+    const dim3 grid(8 * a.per_xcd);
+    const bool cached = (a.chunk + Geo::KT) / a.P + 2 <= Geo::TC;
+    if (cached && a.P % Geo::KT == 0)
+        hipLaunchKernelGGL((part_mfma_kernel<D, G, QW, 0>), grid, dim3(256), 0, st, a);
+    else if (cached)
+        hipLaunchKernelGGL((part_mfma_kernel<D, G, QW, 1>), grid, dim3(256), 0, st, a);
     else
-        hipLaunchKernelGGL((part_mfma_kernel<D, G, false>), grid, dim3(256), 0, st, a);
+        hipLaunchKernelGGL((part_mfma_kernel<D, G, QW, 2>), grid, dim3(256), 0, st, a);
     return hipGetLastError();
 }
 
-hipError_t launch_part_mfma(int D, int G, const PartArgs &a, int S, hipStream_t st) {
-    if (D == 128 && G == 4) return launch_d_g<128, 4>(a, S, st);
-    if (D == 128 && G == 8) return launch_d_g<128, 8>(a, S, st);
-    if (D == 512 && G == 4) return launch_d_g<512, 4>(a, S, st);
-    if (D == 512 && G == 8) return launch_d_g<512, 8>(a, S, st);
+hipError_t launch_part_mfma(int D, int G, const MfmaPlan &p, const PartArgs &args, int S, hipStream_t st) {
+    if (args.chunk != p.chunk || args.chunk % mfma_tile_keys(D) != 0) return hipErrorInvalidValue;
+    PartArgs a = args;
+    a.S = S;
+    a.tiles = p.tiles;
+    const int64_t items = (int64_t)S * a.Hkv * a.n_splits * p.tiles;
+    if (items == 0) return hipSuccess;
+    if (items > (int64_t)1 << 30) return hipErrorInvalidValue;
+    a.per_xcd = (int)((items + 7) / 8);
+    if (p.qw != 1) return hipErrorInvalidValue;
+    if (D == 128 && G == 4) return launch_dgq<128, 4, 1>(a, st);
+    if (D == 128 && G == 8) return launch_dgq<128, 8, 1>(a, st);
+    if (D == 512 && G == 4) return launch_dgq<512, 4, 1>(a, st);
+    if (D == 512 && G == 8) return launch_dgq<512, 8, 1>(a, st);
     return hipErrorInvalidValue;
 }
 

@@ -133,7 +133,8 @@ __global__ __launch_bounds__(64 * valu_waves<NQ>()) void part_valu_kernel(const 
     constexpr int NW = valu_waves<NQ>();
     using Loader = BatchLoader<D, NW>;
     constexpr int NS = Loader::NS;
-    constexpr int PRS = 2 * D + 16;                     // V pair-row stride (bf16 elements)
+    constexpr int PRS = 2 * D + 8;                      // V pair-row stride (bf16 elements): 528 bytes at
+                                                        // D = 128 keeps the PV reads free of bank conflicts
     static_assert(NQ % G == 0 && NQ % VW == 0, "query vectors split evenly over the waves");
 
     // K tile (row-major, rows padded by 16 bytes for conflict-free lane-per-key reads), V tile
