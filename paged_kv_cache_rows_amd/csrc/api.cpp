@@ -105,6 +105,8 @@ kv_status deep_check(const kv_pool *pool, const kv_layout *lay, int64_t ring_spa
 struct Plan {
     bool mfma;
     int D, G, Hkv, Hq, S, R, chunk, n_splits;
+    bool even;   // VALU: even pieces per stream; MFMA: absolute chunks of `chunk` keys
+    int align;
     kvp::MfmaPlan mp;
 };
 
@@ -147,9 +149,22 @@ kv_status make_plan(const kv_pool *pool, const kv_layout *lay, const kv_attn_arg
     } else {
         if (!kvp::valu_supported(p->D, p->G, nq))
             return fail(KV_E_SHAPE, "%s: no VALU kernel for head_dim %d, group %d, rows %d", who, p->D, p->G, p->R);
-        p->chunk = kvp::valu_chunk(p->D);
+        // L - base is at most max_seq_len, or the window plus the rows plus the alignment
+        int span = lay->max_seq_len;
+        const int align = p->D == 512 ? 16 : 64;
+        if (a->window > 0 && (int64_t)a->window + p->R - 1 + align - 1 < span)
+            span = a->window + p->R - 1 + align - 1;
+        const kvp::ValuPlan vp = kvp::valu_plan(p->D, nq, p->S, p->Hkv, span < 1 ? 1 : span);
+        p->chunk = vp.max_piece;
+        p->n_splits = vp.n_splits;
+        p->even = true;
+        p->align = vp.align;
     }
-    p->n_splits = splits_for(lay->max_seq_len, p->R, a->window, p->chunk);
+    if (p->mfma) {
+        p->n_splits = splits_for(lay->max_seq_len, p->R, a->window, p->chunk);
+        p->even = false;
+        p->align = 1;
+    }
     return ok();
 }
 
@@ -213,6 +228,8 @@ kv_status run_attention(const kv_pool *pool, const kv_layout *lay, const kv_attn
     ma.window = a->window;
     ma.n_splits = p.n_splits;
     ma.chunk = p.chunk;
+    ma.even = p.even ? 1 : 0;
+    ma.align = p.align;
     e = kvp::launch_merge(ma, hs);
     if (e != hipSuccess) return fail(KV_E_DEVICE, "%s: merge launch failed: %s", who, hipGetErrorString(e));
     return ok();

@@ -44,11 +44,30 @@ struct MergeArgs {
     const int32_t *seq_len;
     uint16_t *out;   // [S][R][Hq][D]
     int S, R, Hq, D, window, n_splits, chunk;
+    int even;        // 1: splits are the even pieces of split_piece(); 0: chunks of `chunk` keys
+    int align;       // piece granularity of the even split
 };
 
-// Keys per split (workgroup) of each path; split boundaries are multiples of this in absolute
-// positions, so they depend on (L, R, W, D) only and never on physical page ids.
-int valu_chunk(int D);
+// The even split of one stream's keys: the positions a call can see, [lo, L) with lo the
+// lowest first visible key over the call's rows, start at base = lo rounded down to `align`;
+// piece i covers [base + i piece, base + (i + 1) piece) with piece = ceil((L - base) / n)
+// rounded up to `align`.  Every stream gets n pieces of about equal length, so workgroup i of
+// every (stream, head), which the dispatcher places on XCD i mod 8, reads the same number of
+// bytes.  Depends on (L, R, window, n, align) only.
+__host__ __device__ inline int split_base(int L, int R, int window, int align) {
+    const int lo = window > 0 ? (L - R - window + 1 > 0 ? L - R - window + 1 : 0) : 0;
+    return (lo / align) * align;
+}
+__host__ __device__ inline int split_piece(int L, int base, int n, int align) {
+    const int per = (L - base + n - 1) / n;
+    return (per + align - 1) / align * align;
+}
+
+// Splits of a VALU call (about one round of resident workgroups) and the longest piece.
+struct ValuPlan {
+    int n_splits, max_piece, align;
+};
+ValuPlan valu_plan(int D, int NQ, int S, int Hkv, int span);
 bool valu_supported(int D, int G, int NQ);
 bool mfma_supported(int D, int G, int R);
 

@@ -62,13 +62,21 @@ __global__ __launch_bounds__(64) void merge_kernel(const MergeArgs a) {
     for (int c = 0; c < 8; ++c) num[c] = 0.f;
     float den = 0.f, M = -INFINITY;
     if (pos >= 0) {
-        // splits are chunks counted from the first chunk any row of the stream sees; this row
-        // reads only the chunks holding its own keys [lo_r, pos]
-        const int lo_stream = a.window > 0 ? max(0, L - a.R - a.window + 1) : 0;
+        // this row reads only the splits holding its own keys [lo_r, pos]: the even pieces of
+        // the stream, or the chunks counted from the first chunk any row of the stream sees
         const int lo_r = a.window > 0 ? max(0, pos - a.window + 1) : 0;
-        const int first = lo_stream / a.chunk;
-        const int i_begin = lo_r / a.chunk - first;
-        const int n = min(pos / a.chunk - first + 1, a.n_splits);
+        int i_begin, n;
+        if (a.even) {
+            const int base = split_base(L, a.R, a.window, a.align);
+            const int piece = split_piece(L, base, a.n_splits, a.align);
+            i_begin = (lo_r - base) / piece;
+            n = min((pos - base) / piece + 1, a.n_splits);
+        } else {
+            const int lo_stream = a.window > 0 ? max(0, L - a.R - a.window + 1) : 0;
+            const int first = lo_stream / a.chunk;
+            i_begin = lo_r / a.chunk - first;
+            n = min(pos / a.chunk - first + 1, a.n_splits);
+        }
         const float2 *ml = reinterpret_cast<const float2 *>(a.ws_ml) + (size_t)vec * a.n_splits;
         const float *acc = a.ws_acc + (size_t)vec * a.n_splits * D + cb * 8;
         for (int i = i_begin + lane; i < n; i += 64) M = fmaxf(M, ml[i].x);

@@ -35,12 +35,37 @@ struct ValuGeom {
     static constexpr int NB = 16 * RPI;       // keys per batch
     static constexpr int QL = 64 / NB;        // lanes per key in the QK stage
     static constexpr int SEG = D / QL;        // channels per QK lane
-    static constexpr int CHUNK = 16 * NB;     // keys per workgroup
     static constexpr int RS = D + 8;          // LDS row stride (bf16 elements)
-    static constexpr int TC = 72;             // page-table entries cached per chunk
+    static constexpr int TC = 160;            // page-table entries cached per chunk
 };
 
-int valu_chunk(int D) { return D == 512 ? ValuGeom<512>::CHUNK : ValuGeom<128>::CHUNK; }
+// Splits of one call, a function of the call's shape only.  Each stream is cut into n_splits
+// even pieces (split_piece), one workgroup per (stream, KV head, piece).
+//  * n_splits is a multiple of 8 when it is 8 or more: the dispatcher hands workgroups to the
+//    8 XCDs round-robin in grid order, so piece i of every (stream, head) then lands on XCD
+//    i mod 8 and every XCD reads the same number of bytes (measured: 8, 16, 24 or 32 pieces
+//    beat 10 or 12 by 5 to 10 percent on the 12-stream decode).
+//  * About two rounds of resident workgroups (1536 on 256 CUs): every split writes a partial
+//    (D + 2 floats per query vector) that the merge reads back, and that traffic, with the
+//    write-back of the dirty lines when the kernel ends, costs far more than its bytes, so
+//    fewer, longer pieces are better as long as every CU stays busy.
+//  * Pieces of at least 4 batches.
+// `span` bounds L - base over the call's streams.
+ValuPlan valu_plan(int D, int NQ, int S, int Hkv, int span) {
+    (void)NQ;
+    ValuPlan p;
+    p.align = D == 512 ? ValuGeom<512>::NB : ValuGeom<128>::NB;
+    const int64_t target = 1536;
+    const int64_t groups = (int64_t)S * Hkv;
+    int64_t n = (target + groups - 1) / groups;
+    if (n >= 8) n = (n + 7) / 8 * 8;
+    const int64_t most = ((int64_t)span + 4 * p.align - 1) / (4 * p.align);
+    if (n > most) n = most;
+    if (n < 1) n = 1;
+    p.n_splits = (int)n;
+    p.max_piece = split_piece(span, 0, p.n_splits, p.align);
+    return p;
+}
 
 // Loads of one batch.  A batch is 16 load slots t per operand; slot t is rows t*RPI .. +RPI-1
 // (16 bytes per lane).  Wave w owns the contiguous slots [w*NS, w*NS + NS) (NS even, so both
@@ -116,18 +141,19 @@ constexpr int valu_waves() { return NQ / valu_vw<NQ>(); }
 // Load modes, fixed per launch from P: 0 when P is a multiple of the batch, 1 when rows
 // straddle pages but the chunk's table entries fit the LDS cache, 2 for tiny pages.
 template <int D>
-int valu_mode(int P) {
+int valu_mode(int P, int chunk) {
     using Geo = ValuGeom<D>;
-    if (P % Geo::NB == 0) return 0;
-    if ((Geo::CHUNK + Geo::NB) / P + 2 <= Geo::TC && Geo::RPI <= P) return 1;
+    const bool cached = (chunk + Geo::NB) / P + 2 <= Geo::TC;
+    if (cached && P % Geo::NB == 0) return 0;
+    if (cached && Geo::RPI <= P) return 1;
     return 2;
 }
 
 template <int D, int G, int NQ, int MODE>
-__global__ __launch_bounds__(64 * valu_waves<NQ>()) void part_valu_kernel(const PartArgs a) {
+__global__ __launch_bounds__(64 * valu_waves<NQ>()) __attribute__((amdgpu_waves_per_eu(D == 128 && NQ == 8 ? 4 : 1, 8))) void part_valu_kernel(const PartArgs a) {
     using Geo = ValuGeom<D>;
     constexpr int LPR = Geo::LPR, RPI = Geo::RPI, NB = Geo::NB, QL = Geo::QL, SEG = Geo::SEG;
-    constexpr int CHUNK = Geo::CHUNK, RS = Geo::RS, TC = Geo::TC;
+    constexpr int RS = Geo::RS, TC = Geo::TC;
     constexpr int R = NQ / G;
     constexpr int VW = valu_vw<NQ>();                   // query vectors per wave
     constexpr int NW = valu_waves<NQ>();
@@ -152,10 +178,13 @@ __global__ __launch_bounds__(64 * valu_waves<NQ>()) void part_valu_kernel(const 
     const int L = a.seq_len[s];
     const int W = a.window;
     const int lo = W > 0 ? max(0, L - R - W + 1) : 0;
-    const int c0 = (lo / CHUNK + split) * CHUNK;
-    if (L <= 0 || c0 >= L || split >= a.n_splits) return;
+    if (L <= 0 || split >= a.n_splits) return;
+    const int base = split_base(L, R, W, NB);
+    const int piece = split_piece(L, base, a.n_splits, NB);
+    const int c0 = base + split * piece;
+    if (c0 >= L) return;
     const int kbeg = max(c0, lo);
-    const int kend = min(c0 + CHUNK, L);
+    const int kend = min(c0 + piece, L);
 
     // All query vectors of this KV head into LDS: vector v is row v / G, query head kvh*G + v%G.
     // Wave w computes vectors [VW*w, VW*w + VW).
@@ -380,7 +409,8 @@ template <int D, int G, int NQ>
 static hipError_t launch_one(const PartArgs &a, int S, hipStream_t st) {
     constexpr int NW = valu_waves<NQ>();
     const dim3 grid(a.n_splits, a.Hkv, S);
-    switch (valu_mode<D>(a.P)) {
+    if (a.chunk % ValuGeom<D>::NB != 0) return hipErrorInvalidValue;
+    switch (valu_mode<D>(a.P, a.chunk)) {
         case 0: hipLaunchKernelGGL((part_valu_kernel<D, G, NQ, 0>), grid, dim3(64 * NW), 0, st, a); break;
         case 1: hipLaunchKernelGGL((part_valu_kernel<D, G, NQ, 1>), grid, dim3(64 * NW), 0, st, a); break;
         default: hipLaunchKernelGGL((part_valu_kernel<D, G, NQ, 2>), grid, dim3(64 * NW), 0, st, a); break;

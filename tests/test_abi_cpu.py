@@ -201,8 +201,9 @@ def test_workspace_size_depends_on_shape_only(lib):
     n = ctypes.c_size_t()
     lay = binding.Layout(12, 1, 0x30000, 80, 0x40000, 40960, 0)
     assert lib.paged_attn_workspace_size(h, ctypes.byref(lay), ctypes.byref(_args(Hq=64)), ctypes.byref(n)) == 0
-    # 12 streams x 64 heads x 40 splits of 1024 keys x (128 + 2) floats
-    assert n.value == 12 * 64 * 40 * 130 * 4
+    # 12 streams x 8 KV heads = 96 (stream, head) groups and about 1536 workgroups: 16 even
+    # pieces per stream; 12 streams x 64 heads x 16 x (128 + 2) floats
+    assert n.value == 12 * 64 * 16 * 130 * 4
     lib.kv_pool_destroy(h)
 
 
