@@ -94,8 +94,8 @@ struct BatchLoader {
 #pragma unroll
             for (int i = 0; i < NS; ++i) {
                 const int t = min(t0 + i, 15);
-                kr[i] = *reinterpret_cast<const u32x4 *>(k_pages + base + (size_t)(t * RPI) * D);
-                vr[i] = *reinterpret_cast<const u32x4 *>(v_pages + base + (size_t)(t * RPI) * D);
+                kr[i] = stream_load(k_pages + base + (size_t)(t * RPI) * D);
+                vr[i] = stream_load(v_pages + base + (size_t)(t * RPI) * D);
             }
         } else if constexpr (MODE == 1) {
             // rows straddle pages: step RPI rows at a time, crossing at most one boundary
@@ -106,8 +106,8 @@ struct BatchLoader {
             for (int i = 0; i < NS; ++i) {
                 const int pg = max(t_lds[idx - idx0], 0);
                 const size_t e = (size_t)pg * page_elems + head_off + (size_t)off * D;
-                kr[i] = *reinterpret_cast<const u32x4 *>(k_pages + e);
-                vr[i] = *reinterpret_cast<const u32x4 *>(v_pages + e);
+                kr[i] = stream_load(k_pages + e);
+                vr[i] = stream_load(v_pages + e);
                 off += RPI;
                 const bool wrap = off >= P;
                 off = wrap ? off - P : off;
@@ -125,8 +125,8 @@ struct BatchLoader {
                 const int tp = trow[min(idx, stride - 1)];
                 const int pg = (idx < stride && (unsigned)tp < (unsigned)num_pages) ? tp : 0;
                 const size_t e = (size_t)pg * page_elems + head_off + (size_t)off * D;
-                kr[i] = *reinterpret_cast<const u32x4 *>(k_pages + e);
-                vr[i] = *reinterpret_cast<const u32x4 *>(v_pages + e);
+                kr[i] = stream_load(k_pages + e);
+                vr[i] = stream_load(v_pages + e);
             }
         }
     }
