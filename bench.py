@@ -26,7 +26,9 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 METRIC = "paged-attn decode µs/layer + K/V HBM GB/s (% peak), 12 streams x 40k ctx"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "part_valu_d128_g8_batched_decode_traffic.json")
-KERNEL_SOURCE = os.path.join(ROOT, "paged_kv_cache_rows_amd", "csrc", "kernels_valu.hip")
+# the decode part kernel is built from these; counter figures taken on other sources are stale
+KERNEL_SOURCES = [os.path.join(ROOT, "paged_kv_cache_rows_amd", "csrc", f)
+                  for f in ("kernels_valu.hip", "device_common.h", "internal.h")]
 
 
 def log(msg):
@@ -42,12 +44,19 @@ def parse():
     ap.add_argument("--quick", action="store_true", help="skip the side measurements")
     ap.add_argument("--fixed-length", type=int, default=None, help="all 12 streams at this length")
     ap.add_argument("--calib-copy", action="store_true", help="also run a 1 GiB device copy (counter calibration)")
+    ap.add_argument("--side-only", action="store_true",
+                    help="run only the verify, wide-head and prompt workloads (for profiler runs)")
+    ap.add_argument("--no-graphs", action="store_true",
+                    help="time the side workloads with plain launches instead of graph replays")
     return ap.parse_args()
 
 
 def source_digest() -> str:
-    with open(KERNEL_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    h = hashlib.sha256()
+    for path in KERNEL_SOURCES:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def measured_traffic():
@@ -132,10 +141,25 @@ def cold_calls(setup, iters, torch):
     return ms[len(ms) // 2]
 
 
+USE_GRAPHS = True
+
+
 def graph_us(fn, torch, reps=20, iters=5, check=None):
     """GPU time per fn() call in µs: `reps` calls captured into one HIP graph, replayed `iters`
     times between two events, so host-side launch cost does not show.  `check` (a tensor fn
-    writes) is compared byte for byte between the eager call and the last replay."""
+    writes) is compared byte for byte between the eager call and the last replay.  With
+    USE_GRAPHS off, the reps * iters calls are plain launches between the events."""
+    if not USE_GRAPHS:
+        fn()
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps * iters):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e3 / (iters * reps)
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
@@ -302,6 +326,14 @@ def main():
         sys.exit(1)
     binding.load()
     torch.cuda.set_device(0)
+    global USE_GRAPHS
+    USE_GRAPHS = not args.no_graphs
+    if args.side_only:
+        log("[bench] side workloads only")
+        res = {"side_only": True, "graphs": USE_GRAPHS,
+               "other_workloads": other_workloads(torch, binding, staging, workloads)}
+        print(json.dumps(res), flush=True)
+        return
 
     w = workloads.batched_decode(fixed_length=args.fixed_length)
     log(f"[bench] building {w.name}: lengths {w.lengths}, pool {w.pool_pages} pages")
