@@ -205,6 +205,8 @@ kv_status run_attention(const kv_pool *pool, const kv_layout *lay, const kv_attn
     pa.window = a->window;
     pa.n_splits = p.n_splits;
     pa.chunk = p.chunk;
+    pa.out = static_cast<uint16_t *>(a->out);
+    pa.direct = (p.mfma && p.n_splits == 1) ? 1 : 0;
     const float scale = a->scale > 0.f ? a->scale : 1.0f / std::sqrt((float)p.D);
     pa.scale_log2 = scale * 1.4426950408889634f;
 
@@ -215,6 +217,8 @@ kv_status run_attention(const kv_pool *pool, const kv_layout *lay, const kv_attn
     if (e != hipSuccess) return fail(KV_E_DEVICE, "%s: part kernel launch failed: %s", who, hipGetErrorString(e));
     if (g_part_stop && hipEventRecord(g_part_stop, hs) != hipSuccess)
         return fail(KV_E_DEVICE, "%s: recording the stop event failed", who);
+
+    if (pa.direct) return ok();    // the part kernel wrote the output
 
     kvp::MergeArgs ma;
     ma.ws_acc = pa.ws_acc;

@@ -35,6 +35,8 @@ struct PartArgs {
     int chunk;         // keys per split (a multiple of the kernel's key tile)
     int S, tiles;      // streams and query tiles per (stream, KV head) of an MFMA call
     int per_xcd;       // MFMA work items per XCD (the grid is 8 * per_xcd workgroups)
+    uint16_t *out;     // MFMA with n_splits == 1: bf16 output [S][R][Hq][D] written directly
+    int direct;        //   (1), with no partials and no merge; 0: partials into the workspace
     float scale_log2;  // scale * log2(e)
 };
 
@@ -76,6 +78,7 @@ bool mfma_supported(int D, int G, int R);
 // the call's shape only.
 struct MfmaPlan {
     int qw, tiles, chunk;
+    int ks;   // key sub-tiles per step (2: 8-wave workgroups, D = 128 only)
 };
 MfmaPlan mfma_plan(int D, int G, int R, int S, int Hkv, int max_seq_len, int window);
 

@@ -75,12 +75,22 @@ MfmaPlan mfma_plan(int D, int G, int R, int S, int Hkv, int max_seq_len, int win
     // one 16-column block per wave: two (QW = 2) halve the LDS reads per MFMA but need
     // about 280 registers, one wave per SIMD, and measured slower on every workload here
     p.qw = 1;
+    p.ks = 1;
     p.tiles = (nq + 64 * p.qw - 1) / (64 * p.qw);
     const int kt = mfma_tile_keys(D);
     int span = max_seq_len;
     if (window > 0 && (int64_t)window + R - 1 < span) span = window + R - 1;
     if (span < 1) span = 1;
     const int64_t groups = (int64_t)S * Hkv * p.tiles;
+    // enough query tiles to fill the CUs: one split per tile, whose output is then written
+    // directly (partials and their merge cost far more than their bytes: a 512-row prompt
+    // chunk over 2048 keys takes 53 us with 4 splits and a merge, 38 us with one)
+    if (groups >= 256) {
+        p.chunk = (span + kt - 1) / kt * kt;
+        if (p.chunk < kt) p.chunk = kt;
+        p.ks = D == 128 ? 2 : 1;     // 8 waves over two key sub-tiles: half the tile chain
+        return p;
+    }
     // aim at 2 (verify windows, bound by HBM) or 4 (prompt chunks, whose causal triangle
     // leaves part of the grid idle) workgroups per CU over the whole call: long enough chunks
     // to amortise the per-workgroup set-up, short enough to keep every CU busy
@@ -100,8 +110,12 @@ __device__ __forceinline__ f32x4_t mfma16(const bf16x8_t &a, const bf16x8_t &b, 
 
 // MODE 0: P % KT == 0 and the chunk's table entries cached in LDS (one lookup per tile);
 // MODE 1: entries cached, lookup per piece; MODE 2: lookup per piece in the global table.
-template <int D, int G, int QW, int MODE>
-__global__ __launch_bounds__(256) void part_mfma_kernel(const PartArgs a) {
+// KS: key sub-tiles per iteration.  With KS = 2 the workgroup has 8 waves: waves 4 g .. 4 g + 3
+// compute sub-tile g of each 2 KT-key step with an online softmax of their own, and the two
+// states are combined through LDS at the end, which halves the tile chain of a workgroup
+// without splitting the keys over workgroups (no partials in memory).
+template <int D, int G, int QW, int MODE, int KS>
+__global__ __launch_bounds__(256 * KS) void part_mfma_kernel(const PartArgs a) {
     using Geo = MfmaGeom<D>;
     constexpr int KT = Geo::KT, KRS = Geo::KRS, CB = Geo::CB, KPT = Geo::KPT, TC = Geo::TC;
     constexpr int M = 64 * QW;       // query vectors per workgroup
@@ -110,12 +124,17 @@ __global__ __launch_bounds__(256) void part_mfma_kernel(const PartArgs a) {
     constexpr int NCB = D / 16;      // 16-channel blocks (PV output blocks)
     constexpr int NPM = KT / 32;     // 32-key PV k-steps
 
-    __shared__ __attribute__((aligned(16))) uint16_t k_lds[KT * KRS];
-    __shared__ __attribute__((aligned(16))) uint2 vt_lds[D * KT / 4];
+    constexpr int NTH = 256 * KS;    // threads
+    static_assert(KS == 1 || (KS == 2 && D == 128), "key sub-tiles: 1, or 2 at D = 128");
+
+    __shared__ __attribute__((aligned(16))) uint16_t k_lds_all[KS][KT * KRS];
+    __shared__ __attribute__((aligned(16))) uint2 vt_lds_all[KS][D * KT / 4];
     __shared__ int32_t t_lds[TC];
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
+    const int lane = tid & 63;
+    const int wave = (tid >> 6) & 3;          // column wave: query vectors 16 (wave QW + b) + col
+    const int ksub = tid >> 8;                // key sub-tile this wave computes (and thread stages)
     const int col = lane & 15, grp = lane >> 4;
     // work item: the dispatcher hands workgroups to the 8 XCDs round-robin (dispatch id
     // d goes to XCD d mod 8), so XCD x gets the contiguous items [x per, (x + 1) per), ordered
@@ -131,7 +150,7 @@ __global__ __launch_bounds__(256) void part_mfma_kernel(const PartArgs a) {
     const int L = a.seq_len[s];
     const int NQ = R * G;
     const int v0 = tile * M;
-    if (L <= 0 || v0 >= NQ || split >= a.n_splits) return;
+    if (v0 >= NQ || split >= a.n_splits) return;
     const int r_first = v0 / G;
     const int r_last = (min(NQ, v0 + M) - 1) / G;
     const int p_first = L - R + r_first, p_last = L - R + r_last;
@@ -140,7 +159,21 @@ __global__ __launch_bounds__(256) void part_mfma_kernel(const PartArgs a) {
     const int lo_tile = W > 0 ? max(0, p_first - W + 1) : 0;
     const int kbeg = max(c0, lo_tile);
     const int kend = min(c0 + CH, p_last + 1);
-    if (kbeg >= kend) return;        // no row of the tile sees this chunk: nothing to merge
+    if (kbeg >= kend) {
+        // no row of the tile sees this chunk: nothing to merge; a direct call owns the output
+        // of its rows, which are then rows before the start of the stream: zeros
+        if (a.direct && ksub == 0) {
+#pragma unroll
+            for (int b = 0; b < QW; ++b) {
+                const int vq = v0 + (wave * QW + b) * 16 + col;
+                if (vq < NQ) {
+                    uint16_t *dst = a.out + ((size_t)(s * R + vq / G) * a.Hq + kvh * G + vq % G) * D + 4 * grp;
+                    for (int cb = 0; cb < NCB; ++cb) *reinterpret_cast<uint2 *>(dst + 16 * cb) = make_uint2(0u, 0u);
+                }
+            }
+        }
+        return;
+    }
     const int lo_full = W > 0 ? p_last - W + 1 : 0;   // every column sees keys >= this ...
     const int hi_full = p_first;                      // ... and <= this
 
@@ -168,11 +201,11 @@ __global__ __launch_bounds__(256) void part_mfma_kernel(const PartArgs a) {
 
     const int P = a.P;
     const int kt_first = (kbeg / KT) * KT;
-    const int nt = (kend - kt_first + KT - 1) / KT;
+    const int nt = (kend - kt_first + KT - 1) / KT;     // KT-key sub-tiles
     const int idx0 = kt_first / P;
     const int32_t *trow = a.table + (size_t)s * a.stride;
     if (MODE != 2) {
-        for (int i = tid; i < TC; i += Geo::NT) {
+        for (int i = tid; i < TC; i += NTH) {
             int idx = idx0 + i;
             if (a.ring_pages) idx %= a.ring_pages;
             int pg = -1;
@@ -184,8 +217,12 @@ __global__ __launch_bounds__(256) void part_mfma_kernel(const PartArgs a) {
 
     const size_t page_elems = (size_t)a.Hkv * P * D;
     const size_t head_off = (size_t)kvh * P * D;
-    // this thread's pieces: keys KPT kq .. KPT kq + KPT - 1 of a tile, channels 8 kc .. + 8
-    const int kc = tid % CB, kq = tid / CB;
+    // this thread's pieces: keys KPT kq .. KPT kq + KPT - 1 of sub-tile ksub, channels 8 kc .. + 8
+    const int kc = (tid & 255) % CB, kq = (tid & 255) / CB;
+    uint16_t *const k_st = k_lds_all[ksub];   // staged by this thread
+    uint2 *const vt_st = vt_lds_all[ksub];
+    const uint16_t *const k_lds = k_lds_all[ksub];   // computed on by this wave
+    const uint2 *const vt_lds = vt_lds_all[ksub];
     u32x4 kreg0[KPT], vreg0[KPT], kreg1[KPT], vreg1[KPT];
     auto load_tile = [&](int tb, u32x4 (&kreg)[KPT], u32x4 (&vreg)[KPT]) {
         if (MODE == 0) {
@@ -237,21 +274,23 @@ __global__ __launch_bounds__(256) void part_mfma_kernel(const PartArgs a) {
     const int vt_row_l = (col / RPS) * 32;
     const int vt_x_l = ((col % RPS) * Geo::UPR + grp) ^ vt_swz(col / RPS);
 
-    // NPF tiles in flight (2 at d 128; 1 at d 512, where a tile is 8 registers x 4 per
-    // thread and operand): tile it + NPF is loaded into the registers that tile it was staged
-    // from; loads past the last tile reread it (in bounds, never staged), and with NPF = 2 an
-    // odd tile count is padded with one tile whose keys are all masked out
+    // NPF steps in flight (2 at d 128; 1 at d 512, where a tile is 8 registers x 4 per
+    // thread and operand): step it + NPF is loaded into the registers that step it was staged
+    // from.  Step it covers sub-tiles KS it .. KS it + KS - 1; loads past the last sub-tile
+    // reread it (in bounds, never computed on), and sub-tiles past it are all masked out.
     constexpr int NPF = D == 128 ? 2 : 1;
     const int kt_last = kt_first + (nt - 1) * KT;
+    const int nsteps = (nt + KS - 1) / KS;
     auto step = [&](int it, u32x4 (&kreg)[KPT], u32x4 (&vreg)[KPT]) {
-        const int tb = kt_first + it * KT;
+        const int ts = kt_first + (it * KS + (tid >> 8)) * KT;    // sub-tile this thread stages
+        const int tb = kt_first + (it * KS + ksub) * KT;          // sub-tile this wave computes
         lds_fence();
         // stage: K rows as loaded; V transposed into 4-key units, keys outside [kbeg, kend)
         // zeroed (they may be unused slots holding NaN)
 #pragma unroll
         for (int u = 0; u < KPT; ++u)
-            *reinterpret_cast<u32x4 *>(k_lds + (KPT * kq + u) * KRS + 8 * kc) = kreg[u];
-        const bool inside = tb >= kbeg && tb + KT <= kend;
+            *reinterpret_cast<u32x4 *>(k_st + (KPT * kq + u) * KRS + 8 * kc) = kreg[u];
+        const bool inside = ts >= kbeg && ts + KT <= kend;
 #pragma unroll
         for (int h = 0; h < KPT / 4; ++h) {
             u32x4 x[4];
@@ -259,7 +298,7 @@ __global__ __launch_bounds__(256) void part_mfma_kernel(const PartArgs a) {
             for (int u = 0; u < 4; ++u) {
                 x[u] = vreg[4 * h + u];
                 if (!inside) {
-                    const int j = tb + KPT * kq + 4 * h + u;
+                    const int j = ts + KPT * kq + 4 * h + u;
                     const uint32_t keep = (j >= kbeg && j < kend) ? 0xFFFFFFFFu : 0u;
                     x[u] = x[u] & keep;
                 }
@@ -271,11 +310,11 @@ __global__ __launch_bounds__(256) void part_mfma_kernel(const PartArgs a) {
                                             __builtin_amdgcn_perm(x[3][i], x[2][i], 0x05040100u));
                 const uint2 od = make_uint2(__builtin_amdgcn_perm(x[1][i], x[0][i], 0x07060302u),
                                             __builtin_amdgcn_perm(x[3][i], x[2][i], 0x07060302u));
-                vt_lds[vt_unit<D>(8 * kc + 2 * i, kg)] = ev;
-                vt_lds[vt_unit<D>(8 * kc + 2 * i + 1, kg)] = od;
+                vt_st[vt_unit<D>(8 * kc + 2 * i, kg)] = ev;
+                vt_st[vt_unit<D>(8 * kc + 2 * i + 1, kg)] = od;
             }
         }
-        load_tile(min(tb + NPF * KT, kt_last), kreg, vreg);
+        load_tile(min(ts + NPF * KS * KT, kt_last), kreg, vreg);
         lds_fence();
 
         // S^T for this wave's query columns; each K fragment feeds QW MFMAs
@@ -364,26 +403,72 @@ __global__ __launch_bounds__(256) void part_mfma_kernel(const PartArgs a) {
             }
         }
     };
-    load_tile(kt_first, kreg0, vreg0);
+    const int ts0 = kt_first + (tid >> 8) * KT;
+    load_tile(min(ts0, kt_last), kreg0, vreg0);
     if (NPF == 2) {
-        // keep the two first tiles in issue order: the wait counts at the top of the loop
+        // keep the two first steps in issue order: the wait counts at the top of the loop
         // assume buffer 0's loads are older than buffer 1's on every path into it
         asm volatile("" ::: "memory");
-        load_tile(min(kt_first + KT, kt_last), kreg1, vreg1);
-        for (int it = 0; it < nt; it += 2) {
+        load_tile(min(ts0 + KS * KT, kt_last), kreg1, vreg1);
+        for (int it = 0; it < nsteps; it += 2) {
             step(it, kreg0, vreg0);
             step(it + 1, kreg1, vreg1);
         }
     } else {
-        for (int it = 0; it < nt; ++it) step(it, kreg0, vreg0);
+        for (int it = 0; it < nsteps; ++it) step(it, kreg0, vreg0);
     }
 
-    // combine the four key groups' partial sums of each column, write the partials
+    if constexpr (KS == 2) {
+        // combine the two key sub-tile groups: waves 4..7 hand their state to waves 0..3
+        // through LDS (field f of lane (wave, lane) at f * 256 + 64 wave + lane), then only
+        // waves 0..3 go on
+        constexpr int NF = 4 * NCB + 2;
+        static_assert(NF * 256 * 4 <= KS * KT * KRS * 2, "exchange fits the K tiles");
+        float *xch = reinterpret_cast<float *>(&k_lds_all[0][0]);
+        const int xi = 64 * wave + lane;
+        lds_fence();
+        if (ksub == 1) {
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) xch[(4 * cb + r) * 256 + xi] = o[0][cb][r];
+            xch[(4 * NCB) * 256 + xi] = m_run[0];
+            xch[(4 * NCB + 1) * 256 + xi] = l_run[0];
+        }
+        lds_fence();
+        if (ksub == 1) return;
+        const float m1 = xch[(4 * NCB) * 256 + xi];
+        const float l1 = xch[(4 * NCB + 1) * 256 + xi];
+        const float m = fmaxf(m_run[0], m1);
+        const float mc = (m == -INFINITY) ? 0.f : m * c2;
+        const float a0 = m_run[0] == -INFINITY ? 0.f : fast_exp2(m_run[0] * c2 - mc);
+        const float a1 = m1 == -INFINITY ? 0.f : fast_exp2(m1 * c2 - mc);
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) o[0][cb][r] = o[0][cb][r] * a0 + xch[(4 * cb + r) * 256 + xi] * a1;
+        l_run[0] = l_run[0] * a0 + l1 * a1;
+        m_run[0] = m;
+    }
+
+    // combine the four key groups' partial sums of each column; write the normalised bf16
+    // output (a direct call: the one split is the whole result, with the merge's arithmetic)
+    // or the partials
 #pragma unroll
     for (int b = 0; b < QW; ++b) {
         float l_tot = l_run[b] + __shfl_xor(l_run[b], 16);
         l_tot = l_tot + __shfl_xor(l_tot, 32);
-        if (col_ok[b]) {
+        if (a.direct) {
+            if (col_ok[b]) {
+                const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
+                uint16_t *dst = a.out + ((size_t)(s * R + rq[b]) * a.Hq + hq[b]) * D + 4 * grp;
+#pragma unroll
+                for (int cb = 0; cb < NCB; ++cb)
+                    *reinterpret_cast<uint2 *>(dst + 16 * cb) =
+                        make_uint2(pack_bf16x2(o[b][cb][0] * inv, o[b][cb][1] * inv),
+                                   pack_bf16x2(o[b][cb][2] * inv, o[b][cb][3] * inv));
+            }
+        } else if (col_ok[b]) {
             const size_t slot = ((size_t)(s * R + rq[b]) * a.Hq + hq[b]) * a.n_splits + split;
             float *dst = a.ws_acc + slot * D + 4 * grp;
 #pragma unroll
@@ -398,17 +483,17 @@ __global__ __launch_bounds__(256) void part_mfma_kernel(const PartArgs a) {
     }
 }
 
-template <int D, int G, int QW>
+template <int D, int G, int QW, int KS>
 static hipError_t launch_dgq(const PartArgs &a, hipStream_t st) {
     using Geo = MfmaGeom<D>;
     const dim3 grid(8 * a.per_xcd);
     const bool cached = (a.chunk + Geo::KT) / a.P + 2 <= Geo::TC;
     if (cached && a.P % Geo::KT == 0)
-        hipLaunchKernelGGL((part_mfma_kernel<D, G, QW, 0>), grid, dim3(256), 0, st, a);
+        hipLaunchKernelGGL((part_mfma_kernel<D, G, QW, 0, KS>), grid, dim3(256 * KS), 0, st, a);
     else if (cached)
-        hipLaunchKernelGGL((part_mfma_kernel<D, G, QW, 1>), grid, dim3(256), 0, st, a);
+        hipLaunchKernelGGL((part_mfma_kernel<D, G, QW, 1, KS>), grid, dim3(256 * KS), 0, st, a);
     else
-        hipLaunchKernelGGL((part_mfma_kernel<D, G, QW, 2>), grid, dim3(256), 0, st, a);
+        hipLaunchKernelGGL((part_mfma_kernel<D, G, QW, 2, KS>), grid, dim3(256 * KS), 0, st, a);
     return hipGetLastError();
 }
 
@@ -421,11 +506,11 @@ hipError_t launch_part_mfma(int D, int G, const MfmaPlan &p, const PartArgs &arg
     if (items == 0) return hipSuccess;
     if (items > (int64_t)1 << 30) return hipErrorInvalidValue;
     a.per_xcd = (int)((items + 7) / 8);
-    if (p.qw != 1) return hipErrorInvalidValue;
-    if (D == 128 && G == 4) return launch_dgq<128, 4, 1>(a, st);
-    if (D == 128 && G == 8) return launch_dgq<128, 8, 1>(a, st);
-    if (D == 512 && G == 4) return launch_dgq<512, 4, 1>(a, st);
-    if (D == 512 && G == 8) return launch_dgq<512, 8, 1>(a, st);
+    if (p.qw != 1 || (p.ks == 2 && D != 128)) return hipErrorInvalidValue;
+    if (D == 128 && G == 4) return p.ks == 2 ? launch_dgq<128, 4, 1, 2>(a, st) : launch_dgq<128, 4, 1, 1>(a, st);
+    if (D == 128 && G == 8) return p.ks == 2 ? launch_dgq<128, 8, 1, 2>(a, st) : launch_dgq<128, 8, 1, 1>(a, st);
+    if (D == 512 && G == 4) return launch_dgq<512, 4, 1, 1>(a, st);
+    if (D == 512 && G == 8) return launch_dgq<512, 8, 1, 1>(a, st);
     return hipErrorInvalidValue;
 }
 
