@@ -42,7 +42,7 @@ extern "C" {
 typedef enum kv_status {
     KV_OK = 0,
     KV_E_ARG = -1,        /* a null pointer, a negative or inconsistent size, a bad stream id */
-    KV_E_SHAPE = -2,      /* a shape this build has no kernel for (head_dim, GQA group, rows) */
+    KV_E_SHAPE = -2,      /* a shape the library has no kernel for (head_dim, GQA group, rows) */
     KV_E_NO_PAGES = -3,   /* a lease asked for more pages than are free (nothing was leased) */
     KV_E_WORKSPACE = -4,  /* the workspace passed is smaller than paged_attn_workspace_size() */
     KV_E_DEVICE = -5      /* the HIP runtime reported an error for a launch */
@@ -135,8 +135,11 @@ kv_status kv_stream_pages(const kv_pool *pool, int32_t stream, int32_t *ids_out,
 kv_status kv_rows_put(const kv_pool *pool, const kv_layout *lay, const void *k_new,
                       const void *v_new, void *hip_stream);
 
-/* Bytes of workspace that a decode/verify/prefill call with these arguments needs (a
- * function of S, R, Hq, D, the GQA group, max_seq_len and the window only). */
+/* Bytes of workspace that a decode/verify/prefill call with these arguments needs: a function
+ * of the call's shape only (S, R, Hkv, Hq, D, max_seq_len, window), never of the device
+ * lengths or the table.  It holds the split partials (D + 2 floats per query vector and
+ * split).  A call whose query tiles fill the GPU by themselves uses one split and writes its
+ * output directly; it still asks for, and is checked against, this size. */
 kv_status paged_attn_workspace_size(const kv_pool *pool, const kv_layout *lay,
                                     const kv_attn_args *a, size_t *bytes);
 
