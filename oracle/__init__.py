@@ -14,6 +14,10 @@ What it computes (TensorFold PR #1620, paged K/V for Kolibri-1's full layers):
                             verify rows and an optional sliding window, all in float64 (the
                             author's kernel-timing reply: the paged kernels read the same
                             keys as the linear ones, so the result is the linear cache's).
+  * `attention.attend_stream_tree`
+                            the same over a tree-shaped verify window: every key before the
+                            window plus the row's ancestor slots (decode and drafted verify go
+                            through tree attention in the opening description's Reads bullet).
   * `lease.LeaseModel`      the pool's page hand-out and return, as a plain Python model
                             (opening description: every stream leases pages as it grows).
 
@@ -22,12 +26,14 @@ pure Python, closed forms, permutation invariance, a library special case, invar
 see the module docstrings for which pin covers what.
 """
 from .bf16 import bf16_bits_to_f64, f64_to_bf16_bits
-from .attention import attend, attend_stream, visible_range, row_position, kv_head_of
+from .attention import (attend, attend_stream, attend_stream_tree, tree_keys, visible_range, row_position,
+                        kv_head_of)
 from .pages import gather_linear, rows_put, slot_of
 from .lease import LeaseModel, NoPages
 
 __all__ = [
-    "bf16_bits_to_f64", "f64_to_bf16_bits", "attend", "attend_stream", "visible_range",
+    "bf16_bits_to_f64", "f64_to_bf16_bits", "attend", "attend_stream", "attend_stream_tree", "tree_keys",
+    "visible_range",
     "row_position", "kv_head_of", "gather_linear", "rows_put", "slot_of", "LeaseModel",
     "NoPages",
 ]

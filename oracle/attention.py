@@ -83,6 +83,47 @@ def attend_stream(q, k_lin, v_lin, rows: int, window: int = 0, scale=None, lengt
     return out
 
 
+def tree_keys(length: int, rows: int, r: int, mask: int, window: int = 0):
+    """Keys that row r of a tree-shaped verify window sees, in increasing order.
+
+    Draft trees (TensorFold PR #1620: decode and drafted verify go through tree attention) are
+    flattened into the window's R slots with parents before children; slot i sits at position
+    length - rows + i.  Row r sees every key before the window (inside its sliding window, if
+    any) and, of the window's own slots, those i <= r whose bit i is set in `mask` (its
+    ancestors and itself).  A causal chain is mask = 2^(r+1) - 1.
+    """
+    p = row_position(length, rows, r)
+    lo, hi = visible_range(p, window)
+    base = length - rows
+    return [j for j in range(lo, hi) if j < base or (mask >> (j - base)) & 1]
+
+
+def attend_stream_tree(q, k_lin, v_lin, rows: int, masks, window: int = 0, scale=None, length=None):
+    """One stream of a tree-shaped verify window: q [R][Hq][D], k_lin/v_lin [L][Hkv][D] float64,
+    masks[r] the ancestor bits of row r (see tree_keys).  A row that sees no key gets zeros."""
+    q = np.asarray(q, dtype=np.float64)
+    R, Hq, D = q.shape
+    Hkv = k_lin.shape[1]
+    G = Hq // Hkv
+    L = k_lin.shape[0] if length is None else length
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    out = np.zeros((R, Hq, D), dtype=np.float64)
+    for r in range(R):
+        idx = tree_keys(L, R, r, int(masks[r]), window)
+        if not idx:
+            continue
+        for kvh in range(Hkv):
+            K = k_lin[idx, kvh, :]
+            V = v_lin[idx, kvh, :]
+            heads = [h for h in range(Hq) if kv_head_of(h, G) == kvh]
+            s = (q[r, heads, :] @ K.T) * scale
+            s = s - s.max(axis=1, keepdims=True)
+            w = np.exp(s)
+            out[r, heads, :] = (w @ V) / w.sum(axis=1, keepdims=True)
+    return out
+
+
 def attend(q, k_lins, v_lins, lengths, window: int = 0, scale=None):
     """All streams: q [S][R][Hq][D]; k_lins[s], v_lins[s] are [L_s][Hkv][D] (or (array, first)
     tuples for ring tails).  Returns out [S][R][Hq][D] float64."""

@@ -1,0 +1,83 @@
+"""GPU tests of a decode step captured in a HIP graph and replayed while the streams grow.
+
+The launch grid of a call is sized from the host ceiling `max_seq_len` and every stream length
+is read from device memory, so one captured step (kv_rows_put of each stream's new row, then
+paged_attn_decode) stays valid for later lengths up to that ceiling, as long as the pool and the
+page tables stay where they are.  (TensorFold PR #1620, opening description: attaching the paged
+caches drops any step graph captured before them; here the pages never move, so a captured step
+only needs the leases to cover the growth.)
+
+Every replay is compared byte for byte with the same step run eagerly, and with the oracle;
+eager work (updating the lengths, the new rows and the queries) runs between the replays.
+"""
+import pytest
+import torch
+
+from gpu_support import assert_close, new_cache, oracle_from_history, say
+from paged_kv_cache_rows_amd import binding, staging, workloads
+
+pytestmark = pytest.mark.gpu
+
+STEPS = 4
+
+
+def _w():
+    # final lengths; the history before the replayed steps is STEPS rows shorter
+    return workloads.Workload(name="graph", streams=3, kv_heads=2, group=8, head_dim=128, page_size=64,
+                              rows=1, lengths=[900, 403, 1500], spare_frac=0.2, min_spares=2, seed=21)
+
+
+def _rows(hist, lengths, dev):
+    """The row each stream writes at position length - 1, as [S][1][Hkv][D]."""
+    return torch.stack([hist[s][L - 1:L] for s, L in enumerate(lengths)]).to(dev).contiguous()
+
+
+def test_captured_decode_step_replays_as_streams_grow():
+    w = _w()
+    c, _, _ = new_cache(w, history=False)
+    ks, vs = workloads.kv_history(w)
+    start = [L - STEPS for L in w.lengths]
+    staging.write_history(c, ks, vs, upto=start)
+    dev = c.table.device
+    max_len = max(w.lengths)
+
+    # static inputs and outputs of the captured step
+    seq = torch.tensor(start, dtype=torch.int32, device=dev)
+    k_new = _rows(ks, start, dev)
+    v_new = _rows(vs, start, dev)
+    q = workloads.normal_bf16((w.streams, 1, w.q_heads, w.head_dim), 500).to(dev)
+    out = torch.empty_like(q)
+    ws = torch.empty(binding.workspace_size(c.pool, c.table, seq, 1, w.q_heads, max_len), dtype=torch.uint8,
+                     device=dev)
+
+    def step(o):
+        binding.rows_put(c.pool, c.table, seq, k_new, v_new, max_len)
+        binding.decode(c.pool, q, c.table, seq, max_len, out=o, workspace=ws)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step(out)                       # warm-up: rewrites row start - 1 with its own values
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step(out)
+    torch.cuda.synchronize()
+
+    for i in range(STEPS):
+        lengths = [L0 + i + 1 for L0 in start]
+        say(f"replay {i}: lengths {lengths}")
+        seq.copy_(torch.tensor(lengths, dtype=torch.int32))
+        k_new.copy_(_rows(ks, lengths, dev))
+        v_new.copy_(_rows(vs, lengths, dev))
+        q.copy_(workloads.normal_bf16(q.shape, 501 + i))
+        g.replay()
+        torch.cuda.synchronize()
+        got = out.clone()
+        eager = torch.empty_like(q)
+        step(eager)
+        torch.cuda.synchronize()
+        assert torch.equal(got.view(torch.int16), eager.view(torch.int16)), f"replay {i} differs from eager"
+        assert_close(got, oracle_from_history(ks, vs, q, lengths), f"replay {i}")
+    del g

@@ -340,3 +340,143 @@ def test_planted_wrong_scale_turns_pins_red(monkeypatch):
         return real(q, k, v, rows, window, 1.0 / d if scale is None else scale, length)
     monkeypatch.setattr(oatt, "attend_stream", wrong)
     assert not _pins_pass()
+
+
+# ----------------------------------------------------------------------------- tree windows
+def _random_tree(rng, R):
+    """Parents of a draft tree flattened into R window slots, parents before children: slot 0
+    is the pending token (no parent in the window), parent[i] < i."""
+    return [-1] + [int(rng.integers(0, i)) for i in range(1, R)]
+
+
+def _ancestor_set(parent, r):
+    out = {r}
+    while parent[r] >= 0:
+        r = parent[r]
+        out.add(r)
+    return out
+
+
+def brute_tree_attention(q, k, v, L, R, anc, window=0):
+    """Pure Python over one stream; row r sees key j iff j <= its slot, j is inside the window,
+    and j lies before the window or is one of r's ancestor slots (given as sets, not bits)."""
+    Hq, D, Hkv = len(q[0]), len(q[0][0]), len(k[0])
+    c = 1.0 / math.sqrt(D)
+    out = []
+    for r in range(R):
+        pos = L - R + r
+        rows = []
+        for h in range(Hq):
+            g = (h * Hkv) // Hq
+            keys = [j for j in range(L) if j <= pos and (window <= 0 or j > pos - window)
+                    and (j < L - R or (j - (L - R)) in anc[r])]
+            if not keys:
+                rows.append([0.0] * D)
+                continue
+            sc = [c * math.fsum(q[r][h][d] * k[j][g][d] for d in range(D)) for j in keys]
+            top = max(sc)
+            w = [math.exp(x - top) for x in sc]
+            tot = math.fsum(w)
+            rows.append([math.fsum(w[i] * v[keys[i]][g][d] for i in range(len(keys))) / tot for d in range(D)])
+        out.append(rows)
+    return np.array(out)
+
+
+def _tree_case(seed):
+    rng = np.random.default_rng(seed)
+    R = int(rng.integers(2, 9))
+    Hkv = int(rng.integers(1, 3))
+    G = int(rng.choice([1, 2, 4]))
+    D = int(rng.choice([1, 3, 8]))
+    L = int(rng.integers(R, 30))
+    window = int(rng.choice([0, 0, 2, 5]))
+    parent = _random_tree(rng, R)
+    anc = [_ancestor_set(parent, r) for r in range(R)]
+    masks = [sum(1 << i for i in a) for a in anc]
+    q = rng.standard_normal((R, Hkv * G, D))
+    k = rng.standard_normal((L, Hkv, D))
+    v = rng.standard_normal((L, Hkv, D))
+    return q, k, v, L, R, anc, masks, window
+
+
+def _tree_pins_pass():
+    for seed in range(6):
+        q, k, v, L, R, anc, masks, window = _tree_case(seed)
+        got = oracle.attend_stream_tree(q, k, v, R, masks, window)
+        want = brute_tree_attention(q.tolist(), k.tolist(), v.tolist(), L, R, anc, window)
+        if not np.allclose(got, want, rtol=1e-12, atol=1e-13):
+            return False
+    return True
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_tree_oracle_matches_brute_force(seed):
+    q, k, v, L, R, anc, masks, window = _tree_case(seed)
+    got = oracle.attend_stream_tree(q, k, v, R, masks, window)
+    want = brute_tree_attention(q.tolist(), k.tolist(), v.tolist(), L, R, anc, window)
+    np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-13)
+
+
+def test_chain_tree_equals_causal_verify():
+    rng = np.random.default_rng(3)
+    R, L = 8, 40
+    q = rng.standard_normal((R, 8, 16))
+    k = rng.standard_normal((L, 2, 16))
+    v = rng.standard_normal((L, 2, 16))
+    chain = [(1 << (r + 1)) - 1 for r in range(R)]
+    np.testing.assert_allclose(oracle.attend_stream_tree(q, k, v, R, chain), oracle.attend_stream(q, k, v, R),
+                               rtol=1e-13, atol=1e-14)
+
+
+def test_tree_bits_above_the_row_are_ignored():
+    rng = np.random.default_rng(4)
+    R, L = 6, 25
+    q = rng.standard_normal((R, 4, 8))
+    k = rng.standard_normal((L, 1, 8))
+    v = rng.standard_normal((L, 1, 8))
+    everything = [0xFF] * R
+    np.testing.assert_allclose(oracle.attend_stream_tree(q, k, v, R, everything), oracle.attend_stream(q, k, v, R),
+                               rtol=1e-13, atol=1e-14)
+
+
+def test_tree_row_seeing_only_itself_is_a_decode_without_the_other_drafts():
+    rng = np.random.default_rng(5)
+    R, L, r = 5, 30, 3
+    q = rng.standard_normal((R, 4, 8))
+    k = rng.standard_normal((L, 2, 8))
+    v = rng.standard_normal((L, 2, 8))
+    masks = [(1 << (i + 1)) - 1 for i in range(R)]
+    masks[r] = 1 << r
+    got = oracle.attend_stream_tree(q, k, v, R, masks)[r]
+    keep = list(range(L - R)) + [L - R + r]             # the prefix and the row's own slot
+    want = oracle.attend_stream(q[r:r + 1], k[keep], v[keep], 1)[0]
+    np.testing.assert_allclose(got, want, rtol=1e-13, atol=1e-14)
+
+
+def test_tree_row_with_no_visible_key_is_zero():
+    q = np.ones((2, 2, 4))
+    k = np.ones((2, 1, 4))
+    v = np.ones((2, 1, 4))
+    out = oracle.attend_stream_tree(q, k, v, 2, [0b01, 0b00])     # L == R: no prefix; row 1 sees nothing
+    assert np.all(out[1] == 0) and np.allclose(out[0], 1.0)
+
+
+def test_planted_reversed_tree_bits_turn_pins_red(monkeypatch):
+    assert _tree_pins_pass()
+    real = oatt.tree_keys
+
+    def reversed_bits(length, rows, r, mask, window=0):
+        flipped = sum(((mask >> i) & 1) << (rows - 1 - i) for i in range(rows))
+        return real(length, rows, r, flipped, window)
+    monkeypatch.setattr(oatt, "tree_keys", reversed_bits)
+    assert not _tree_pins_pass()
+
+
+def test_planted_tree_without_the_prefix_turns_pins_red(monkeypatch):
+    assert _tree_pins_pass()
+    real = oatt.tree_keys
+
+    def no_prefix(length, rows, r, mask, window=0):
+        return [j for j in real(length, rows, r, mask, window) if j >= length - rows]
+    monkeypatch.setattr(oatt, "tree_keys", no_prefix)
+    assert not _tree_pins_pass()
