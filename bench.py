@@ -201,8 +201,10 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0
 
 
 def other_workloads(torch, binding, staging, workloads):
-    """The verify window, the wide-head pair and the prompt chunks, timed on their own as GPU
-    time per call (HIP graph replays, so host launch cost does not show)."""
+    """The verify window (causal and as a draft tree), the wide-head pair and the prompt chunks,
+    timed on their own as GPU time per call (HIP graph replays, so host launch cost does not
+    show)."""
+    import numpy as np
     res = {}
     # speculative verify window: 4 streams x 8 rows x ~9k, GQA 8 (MFMA path)
     w = workloads.verify_window()
@@ -222,6 +224,22 @@ def other_workloads(torch, binding, staging, workloads):
                                        "TFLOPs": round(fl / us / 1e6, 2),
                                        "mfma_frac": round(fl / us / 1e6 / MFMA_BF16_PEAK_TFLOPS, 4),
                                        "kv_bytes": by, "flops": fl}
+    # the same window as a flattened draft tree (seeded random trees, parents before children)
+    rng = np.random.default_rng(3103)
+    masks = np.zeros((w.streams, w.rows), dtype=np.int32)
+    for s_ in range(w.streams):
+        parent = [-1] + [int(rng.integers(0, i)) for i in range(1, w.rows)]
+        for r in range(w.rows):
+            m, i = 0, r
+            while i >= 0:
+                m |= 1 << i
+                i = parent[i]
+            masks[s_, r] = m
+    tm = torch.from_numpy(masks).to("cuda")
+    us_t = graph_us(lambda: binding.verify_tree(c.pool, q, c.table, c.seq_len, c.max_seq_len, tm, out=out,
+                                                workspace=ws), torch, check=out)
+    res["verify_tree_4x8rows_9k"] = {"us": round(us_t, 2), "kv_GBps": round(by / us_t / 1e3, 1),
+                                     "hbm_frac": round(by / us_t / 1e3 / HBM_PEAK_GBS, 4)}
     del c, ks, vs
     # wide head: d 512, pages of 37; stream 0 decodes at 2048, stream 1 verifies 4 rows at 9000
     w = workloads.wide_head()

@@ -161,6 +161,17 @@ kv_status paged_attn_decode(const kv_pool *pool, const kv_layout *lay, const kv_
 kv_status paged_attn_verify(const kv_pool *pool, const kv_layout *lay, const kv_attn_args *a,
                             void *hip_stream);
 
+/* The same for a verify window whose R (1..8) rows are a flattened draft tree rather than a
+ * chain (TensorFold PR #1620, opening description, Reads bullet: decode and drafted verify go
+ * through tree attention).  tree_mask: device uint32 [S][R], caller-owned; bit i of
+ * tree_mask[s][r] says that row r of stream s sees window slot i (position L-R+i): its
+ * ancestors and, normally, itself.  The tree must list parents before children; bits above r
+ * are ignored.  Every row sees all keys before the window (inside its sliding window, if any).
+ * A row that sees no key gets zeros.  With tree_mask[s][r] = 2^(r+1) - 1 the result is
+ * paged_attn_verify's, byte for byte.  Errors as for verify, with KV_E_ARG for a null mask. */
+kv_status paged_attn_verify_tree(const kv_pool *pool, const kv_layout *lay, const kv_attn_args *a,
+                                 const uint32_t *tree_mask, void *hip_stream);
+
 /* The same for a prompt chunk of any R >= 1 causal rows per stream (TensorFold PR #1620,
  * opening description, Reads bullet: prompts have paged prompt kernels of their own).  A prompt is
  * processed chunk by chunk: kv_rows_put the chunk's rows, then this call with R = chunk rows.

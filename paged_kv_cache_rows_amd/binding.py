@@ -26,7 +26,8 @@ STATUS_NAMES = {0: "KV_OK", -1: "KV_E_ARG", -2: "KV_E_SHAPE", -3: "KV_E_NO_PAGES
 # The entry points include/kvpaged.h declares (checked against the built library's exports).
 EXPORTS = ("kv_pool_create", "kv_pool_destroy", "kv_page_lease", "kv_page_release",
            "kv_pool_free_count", "kv_stream_pages", "kv_rows_put", "paged_attn_workspace_size",
-           "paged_attn_decode", "paged_attn_verify", "paged_attn_prefill", "kv_set_part_events",
+           "paged_attn_decode", "paged_attn_verify", "paged_attn_verify_tree", "paged_attn_prefill",
+           "kv_set_part_events",
            "kv_last_error", "kv_abi_version")
 
 
@@ -76,6 +77,7 @@ def load(path: str = LIB_PATH):
         "paged_attn_workspace_size": [c_void_p, POINTER(Layout), POINTER(AttnArgs), POINTER(c_size_t)],
         "paged_attn_decode": [c_void_p, POINTER(Layout), POINTER(AttnArgs), c_void_p],
         "paged_attn_verify": [c_void_p, POINTER(Layout), POINTER(AttnArgs), c_void_p],
+        "paged_attn_verify_tree": [c_void_p, POINTER(Layout), POINTER(AttnArgs), c_void_p, c_void_p],
         "paged_attn_prefill": [c_void_p, POINTER(Layout), POINTER(AttnArgs), c_void_p],
         "kv_set_part_events": [c_void_p, c_void_p],
     }
@@ -215,7 +217,8 @@ def workspace_size(pool: Pool, table: torch.Tensor, seq_len: torch.Tensor, rows:
 
 def _attend(entry: str, pool: Pool, q: torch.Tensor, table: torch.Tensor, seq_len: torch.Tensor,
             max_seq_len: int, window: int = 0, ring_pages: int = 0, scale: float = 0.0,
-            out: torch.Tensor | None = None, workspace: torch.Tensor | None = None, stream=None):
+            out: torch.Tensor | None = None, workspace: torch.Tensor | None = None, stream=None,
+            extra=()):
     if q.dim() != 4 or q.shape[3] != pool.head_dim:
         raise ValueError("q must be [S][R][Hq][D]")
     _need(q, torch.bfloat16, "q")
@@ -229,7 +232,8 @@ def _attend(entry: str, pool: Pool, q: torch.Tensor, table: torch.Tensor, seq_le
         workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=q.device)
     args = AttnArgs(_ptr(q), _ptr(out), Hq, float(scale), int(window), _ptr(workspace),
                     int(workspace.numel() * workspace.element_size()))
-    _check(getattr(load(), entry)(pool.handle, ctypes.byref(lay), ctypes.byref(args), _stream_handle(stream)))
+    _check(getattr(load(), entry)(pool.handle, ctypes.byref(lay), ctypes.byref(args), *extra,
+                                  _stream_handle(stream)))
     return out
 
 
@@ -241,6 +245,13 @@ def decode(pool, q, table, seq_len, max_seq_len, **kw):
 def verify(pool, q, table, seq_len, max_seq_len, **kw):
     """paged_attn_verify: 1..8 causal rows per stream."""
     return _attend("paged_attn_verify", pool, q, table, seq_len, max_seq_len, **kw)
+
+
+def verify_tree(pool, q, table, seq_len, max_seq_len, tree_mask: torch.Tensor, **kw):
+    """paged_attn_verify_tree: 1..8 rows per stream forming a flattened draft tree;
+    tree_mask is a device int32 [S][R] of ancestor bits (bit i of row r: r sees slot i)."""
+    _need(tree_mask, torch.int32, "tree_mask", (int(q.shape[0]), int(q.shape[1])))
+    return _attend("paged_attn_verify_tree", pool, q, table, seq_len, max_seq_len, extra=(_ptr(tree_mask),), **kw)
 
 
 def prefill(pool, q, table, seq_len, max_seq_len, **kw):

@@ -173,7 +173,7 @@ size_t workspace_bytes(const Plan &p) {
 }
 
 kv_status run_attention(const kv_pool *pool, const kv_layout *lay, const kv_attn_args *a, void *hip_stream,
-                        const char *who) {
+                        const char *who, const uint32_t *tree = nullptr) {
     Plan p;
     kv_status st = make_plan(pool, lay, a, &p, who);
     if (st != KV_OK) return st;
@@ -206,6 +206,7 @@ kv_status run_attention(const kv_pool *pool, const kv_layout *lay, const kv_attn
     pa.n_splits = p.n_splits;
     pa.chunk = p.chunk;
     pa.out = static_cast<uint16_t *>(a->out);
+    pa.tree = tree;
     pa.direct = (p.mfma && p.n_splits == 1) ? 1 : 0;
     const float scale = a->scale > 0.f ? a->scale : 1.0f / std::sqrt((float)p.D);
     pa.scale_log2 = scale * 1.4426950408889634f;
@@ -385,6 +386,14 @@ kv_status paged_attn_verify(const kv_pool *pool, const kv_layout *lay, const kv_
     if (lay && (lay->rows < 1 || lay->rows > 8))
         return fail(KV_E_ARG, "paged_attn_verify: rows %d outside 1..8", lay->rows);
     return run_attention(pool, lay, a, hip_stream, "paged_attn_verify");
+}
+
+kv_status paged_attn_verify_tree(const kv_pool *pool, const kv_layout *lay, const kv_attn_args *a,
+                                 const uint32_t *tree_mask, void *hip_stream) {
+    if (lay && (lay->rows < 1 || lay->rows > 8))
+        return fail(KV_E_ARG, "paged_attn_verify_tree: rows %d outside 1..8", lay->rows);
+    if (!tree_mask) return fail(KV_E_ARG, "paged_attn_verify_tree: tree_mask is null");
+    return run_attention(pool, lay, a, hip_stream, "paged_attn_verify_tree", tree_mask);
 }
 
 kv_status paged_attn_prefill(const kv_pool *pool, const kv_layout *lay, const kv_attn_args *a, void *hip_stream) {

@@ -35,6 +35,8 @@ struct PartArgs {
     int chunk;         // keys per split (a multiple of the kernel's key tile)
     int S, tiles;      // streams and query tiles per (stream, KV head) of an MFMA call
     int per_xcd;       // MFMA work items per XCD (the grid is 8 * per_xcd workgroups)
+    const uint32_t *tree;  // NULL, or [S][R] ancestor bits of a tree-shaped verify window:
+                           // row r sees window slot i (i <= r) only if bit i is set
     uint16_t *out;     // MFMA with n_splits == 1: bf16 output [S][R][Hq][D] written directly
     int direct;        //   (1), with no partials and no merge; 0: partials into the workspace
     float scale_log2;  // scale * log2(e)

@@ -175,12 +175,15 @@ __global__ __launch_bounds__(256 * KS) void part_mfma_kernel(const PartArgs a) {
         return;
     }
     const int lo_full = W > 0 ? p_last - W + 1 : 0;   // every column sees keys >= this ...
-    const int hi_full = p_first;                      // ... and <= this
+    // ... and <= this (with a tree-shaped window, only the keys before the window)
+    const int hi_full = a.tree ? min(p_first, L - R - 1) : p_first;
+    const int win0 = L - R;                           // first slot of the window
 
     // this lane's query columns, and the queries as the B operand of S^T = K Q^T: the lane
     // holds channels 32 kb + 8 grp .. + 8 of its column
     bool col_ok[QW];
     int rq[QW], hq[QW], p_col[QW], lo_col[QW];
+    uint32_t anc[QW];                                 // ancestor bits of the column's row
     bf16x8_t qf[QW][NKB];
 #pragma unroll
     for (int b = 0; b < QW; ++b) {
@@ -190,6 +193,7 @@ __global__ __launch_bounds__(256 * KS) void part_mfma_kernel(const PartArgs a) {
         hq[b] = kvh * G + (col_ok[b] ? vq % G : 0);
         p_col[b] = L - R + rq[b];
         lo_col[b] = W > 0 ? p_col[b] - W + 1 : 0;
+        anc[b] = a.tree ? a.tree[s * R + rq[b]] : 0xFFFFFFFFu;
         const uint16_t *qrow = a.q + ((size_t)(s * R + rq[b]) * a.Hq + hq[b]) * D + 8 * grp;
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) {
@@ -347,7 +351,9 @@ __global__ __launch_bounds__(256 * KS) void part_mfma_kernel(const PartArgs a) {
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
                         const int j = tb + 16 * nb + 4 * grp + r;
-                        const bool vis = col_ok[b] && j >= kbeg && j < kend && j <= p_col[b] && j >= lo_col[b];
+                        const int t = j - win0;             // window slot of the key, if >= 0
+                        const bool vis = col_ok[b] && j >= kbeg && j < kend && j <= p_col[b] && j >= lo_col[b] &&
+                                         (t < 0 || ((anc[b] >> (t & 31)) & 1u));
                         const float x = vis ? sacc[b][nb][r] : -INFINITY;
                         sacc[b][nb][r] = x;
                         tmax = fmaxf(tmax, x);

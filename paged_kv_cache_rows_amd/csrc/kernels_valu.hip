@@ -233,7 +233,12 @@ __global__ __launch_bounds__(64 * valu_waves<NQ>()) __attribute__((amdgpu_waves_
     const int seg = (QL == 1) ? 0 : (lane / NB);       // its channel segment
     const float scale_log2 = a.scale_log2;
     // keys every row of the call sees: up to row 0's own position, and inside every window
-    const int all_hi = L - R + 1;
+    // (with a tree-shaped window, only the keys before the window: a row may skip slot 0)
+    const int all_hi = a.tree ? L - R : L - R + 1;
+    const int win0 = L - R;                              // first slot of the window
+    uint32_t anc[VW];                                    // ancestor bits of each vector's row
+#pragma unroll
+    for (int v = 0; v < VW; ++v) anc[v] = a.tree ? a.tree[s * R + (VW * wave + v) / G] : 0xFFFFFFFFu;
     const int all_lo = W > 0 ? L - W : 0;
     uint32_t *p_mine = p_lds[wave];
     const uint16_t *qb = q_lds + (VW * wave) * RS + seg * SEG;
@@ -307,7 +312,9 @@ __global__ __launch_bounds__(64 * valu_waves<NQ>()) __attribute__((amdgpu_waves_
             for (int v = 0; v < VW; ++v) {
                 const int pr = L - R + (VW * wave + v) / G;   // position of this vector's row
                 const int lor = W > 0 ? pr - W + 1 : 0;
-                const bool vis = j >= kbeg && j < kend && j <= pr && j >= lor;
+                const int t = j - win0;                     // window slot of the key, if >= 0
+                const bool vis = j >= kbeg && j < kend && j <= pr && j >= lor &&
+                                 (t < 0 || ((anc[v] >> (t & 31)) & 1u));
                 x[v] = vis ? sc[v] * scale_log2 : -INFINITY;
             }
         }

@@ -49,6 +49,36 @@ def oracle_for(cache, q: torch.Tensor, window: int = 0, streams=None, kbits=None
     return np.stack(outs)
 
 
+def oracle_tree_for(cache, q: torch.Tensor, masks, window: int = 0):
+    """Oracle output [S][R][Hq][D] of a tree-shaped verify window (masks [S][R] ancestor bits),
+    gathering each stream's linear cache from host copies of the GPU pool."""
+    kbits, vbits = pool_bits(cache)
+    qb = workloads.bf16_bits(q)
+    outs = []
+    for s in range(cache.w.streams):
+        L = cache.lengths[s]
+        kl = oracle.bf16_bits_to_f64(oracle.gather_linear(kbits, cache.table_host[s], L, cache.w.page_size))
+        vl = oracle.bf16_bits_to_f64(oracle.gather_linear(vbits, cache.table_host[s], L, cache.w.page_size))
+        qs = oracle.bf16_bits_to_f64(qb[s])
+        outs.append(oracle.attend_stream_tree(qs, kl, vl, qs.shape[0], [int(m) for m in masks[s]], window,
+                                              length=L))
+    return np.stack(outs)
+
+
+def random_tree_masks(rng, streams: int, rows: int):
+    """Ancestor bits [S][R] of random draft trees, parents before children (parent[i] < i)."""
+    out = np.zeros((streams, rows), dtype=np.int64)
+    for s in range(streams):
+        parent = [-1] + [int(rng.integers(0, i)) for i in range(1, rows)]
+        for r in range(rows):
+            m, i = 0, r
+            while i >= 0:
+                m |= 1 << i
+                i = parent[i]
+            out[s, r] = m
+    return out
+
+
 def oracle_from_history(ks, vs, q: torch.Tensor, lengths, window=0, streams=None):
     """Oracle output from the generator's history tensors directly (for ring layers, whose
     pool no longer holds the old positions)."""

@@ -217,3 +217,16 @@ def test_rows_put_refuses_bad_layouts(lib):
     assert lib.kv_rows_put(h, ctypes.byref(_layout(ring=1, R=65, max_len=300)), 0x1000, 0x2000, None) == binding.KV_E_ARG
     assert lib.kv_rows_put(None, ctypes.byref(_layout()), 0x1000, 0x2000, None) == binding.KV_E_ARG
     lib.kv_pool_destroy(h)
+
+
+@host_only
+def test_verify_tree_refuses_before_launch(lib):
+    d = binding.PoolDesc(8, 64, 4, 128, 2, 0x10000, 0x20000, None)
+    h = ctypes.c_void_p()
+    assert lib.kv_pool_create(ctypes.byref(d), ctypes.byref(h)) == 0
+    f = lib.paged_attn_verify_tree
+    assert f(h, ctypes.byref(_layout(R=4)), ctypes.byref(_args()), None, None) == binding.KV_E_ARG     # no mask
+    assert f(h, ctypes.byref(_layout(R=9)), ctypes.byref(_args()), 0x80000, None) == binding.KV_E_ARG  # R > 8
+    assert f(h, ctypes.byref(_layout(R=4)), ctypes.byref(_args(Hq=12)), 0x80000, None) == binding.KV_E_SHAPE
+    assert lib.kv_last_error()
+    lib.kv_pool_destroy(h)
