@@ -285,6 +285,34 @@ def other_workloads(torch, binding, staging, workloads):
     return res
 
 
+def kept_state_copy(setup, torch, binding, iters=20):
+    """Keep the state of the longest stream: copy its pages onto spare pages of the pool
+    (kv_pages_copy), timed with HIP events; the copy reads and writes every byte once."""
+    import numpy as np
+    c, w = setup.c, setup.w
+    s = int(np.argmax(c.lengths))
+    n = -(-c.lengths[s] // w.page_size)
+    used = set(int(x) for x in c.table_host[c.table_host >= 0].ravel())
+    spare = [i for i in range(w.pool_pages) if i not in used][:n]
+    if len(spare) < n:
+        return None
+    src = torch.tensor(c.table_host[s][:n], dtype=torch.int32, device="cuda")
+    dst = torch.tensor(spare, dtype=torch.int32, device="cuda")
+    binding.pages_copy(c.pool, src, dst)
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(iters):
+        binding.pages_copy(c.pool, src, dst)
+    b.record()
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) * 1e3 / iters
+    moved = 2 * n * 2 * w.kv_heads * w.page_size * w.head_dim * 2       # K and V, read and written
+    return {"stream_tokens": c.lengths[s], "pages": n, "bytes_moved": moved, "us": round(us, 2),
+            "GBps": round(moved / us / 1e3, 1)}
+
+
 def calibration_copy(torch, nbytes=1 << 30, reps=3):
     """An elementwise kernel of known traffic (reads nbytes, writes nbytes: bitwise_not over
     int32), so that profiler byte counters can be scaled against it.  A plain copy_ may go to
@@ -406,6 +434,8 @@ def main():
         lms, lpart, _, _ = timed_steps(lin, max(20, args.steps // 4), 5, torch, binding)
         result["identity_table"] = {"us_per_layer": round(lms * 1e3, 2), "part_us_mean": round(lpart * 1e3, 2),
                                     "paged_over_identity": round(part_ms / lpart, 4)}
+        log("[bench] kept-state page copy")
+        result["kept_state_copy"] = kept_state_copy(setup, torch, binding)
         same = torch.equal(lin.out.view(torch.int16), setup.out.view(torch.int16))
         result["identity_table"]["bytes_equal"] = bool(same)
         del lin

@@ -135,6 +135,18 @@ kv_status kv_stream_pages(const kv_pool *pool, int32_t stream, int32_t *ids_out,
 kv_status kv_rows_put(const kv_pool *pool, const kv_layout *lay, const void *k_new,
                       const void *v_new, void *hip_stream);
 
+/* Copy whole pages, K and V, every KV head: page dst_ids[i] receives the contents of page
+ * src_ids[i] for i < n (TensorFold PR #1620, opening description, Kept states bullet: a
+ * stream's state is kept by copying the pages its table walks).  Keeping a state: lease fresh
+ * pages, copy the stream's table entries onto them, and the new ids form a table that reads
+ * back the same cache; resuming is attending (and writing) through that table.
+ * src_ids, dst_ids: device int32 [n], caller-owned.  No page may be a destination twice or be
+ * both a source and a destination (the pairs run concurrently); ids outside [0, num_pages)
+ * are skipped.  With KVP_CHECK=1 the ids are copied to the host first and both rules are
+ * checked (KV_E_ARG).  Errors: KV_E_ARG (null pointers, n < 0). */
+kv_status kv_pages_copy(const kv_pool *pool, const int32_t *src_ids, const int32_t *dst_ids, int32_t n,
+                        void *hip_stream);
+
 /* Bytes of workspace that a decode/verify/prefill call with these arguments needs: a function
  * of the call's shape only (S, R, Hkv, Hq, D, max_seq_len, window), never of the device
  * lengths or the table.  It holds the split partials (D + 2 floats per query vector and

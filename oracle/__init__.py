@@ -10,6 +10,8 @@ What it computes (TensorFold PR #1620, paged K/V for Kolibri-1's full layers):
                             per-stream page table).
   * `pages.rows_put`        scatters a call's new K/V rows into their page slots
                             (opening description, Writes bullet).
+  * `pages.copy_pages`      copies whole pages between ids (Kept states bullet: a stream's
+                            state is kept by copying the pages its table walks).
   * `attention.attend`      softmax(q k^T / sqrt(d)) v over the linear cache, with GQA, causal
                             verify rows and an optional sliding window, all in float64 (the
                             author's kernel-timing reply: the paged kernels read the same
@@ -28,12 +30,12 @@ see the module docstrings for which pin covers what.
 from .bf16 import bf16_bits_to_f64, f64_to_bf16_bits
 from .attention import (attend, attend_stream, attend_stream_tree, tree_keys, visible_range, row_position,
                         kv_head_of)
-from .pages import gather_linear, rows_put, slot_of
+from .pages import copy_pages, gather_linear, rows_put, slot_of
 from .lease import LeaseModel, NoPages
 
 __all__ = [
     "bf16_bits_to_f64", "f64_to_bf16_bits", "attend", "attend_stream", "attend_stream_tree", "tree_keys",
     "visible_range",
-    "row_position", "kv_head_of", "gather_linear", "rows_put", "slot_of", "LeaseModel",
+    "row_position", "kv_head_of", "copy_pages", "gather_linear", "rows_put", "slot_of", "LeaseModel",
     "NoPages",
 ]

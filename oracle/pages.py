@@ -60,3 +60,17 @@ def rows_put(pages, table_row, length: int, rows_new, page_size: int, ring_pages
         pg, sl = slot_of(j, table_row, page_size, ring_pages)
         out[pg, :, sl, :] = rows_new[r]
     return out
+
+
+def copy_pages(pages, src_ids, dst_ids, num_pages=None):
+    """Return a copy of pages [N][Hkv][P][D] in which page dst_ids[i] holds what page src_ids[i]
+    held, for every i whose two ids are inside the pool (kept states: a stream's state is kept
+    by copying the pages its table lists, opening description, Kept states bullet).  Copies
+    are taken from the pages as they were before any copy of the call."""
+    src = np.asarray(pages)
+    out = np.array(src, copy=True)
+    n = src.shape[0] if num_pages is None else num_pages
+    for a, b in zip(src_ids, dst_ids):
+        if 0 <= int(a) < n and 0 <= int(b) < n:
+            out[int(b)] = src[int(a)]
+    return out

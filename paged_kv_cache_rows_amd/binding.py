@@ -25,7 +25,7 @@ STATUS_NAMES = {0: "KV_OK", -1: "KV_E_ARG", -2: "KV_E_SHAPE", -3: "KV_E_NO_PAGES
 
 # The entry points include/kvpaged.h declares (checked against the built library's exports).
 EXPORTS = ("kv_pool_create", "kv_pool_destroy", "kv_page_lease", "kv_page_release",
-           "kv_pool_free_count", "kv_stream_pages", "kv_rows_put", "paged_attn_workspace_size",
+           "kv_pool_free_count", "kv_stream_pages", "kv_rows_put", "kv_pages_copy", "paged_attn_workspace_size",
            "paged_attn_decode", "paged_attn_verify", "paged_attn_verify_tree", "paged_attn_prefill",
            "kv_set_part_events",
            "kv_last_error", "kv_abi_version")
@@ -74,6 +74,7 @@ def load(path: str = LIB_PATH):
         "kv_pool_free_count": [c_void_p, i32p],
         "kv_stream_pages": [c_void_p, c_int32, i32p, c_int32, i32p],
         "kv_rows_put": [c_void_p, POINTER(Layout), c_void_p, c_void_p, c_void_p],
+        "kv_pages_copy": [c_void_p, c_void_p, c_void_p, c_int32, c_void_p],
         "paged_attn_workspace_size": [c_void_p, POINTER(Layout), POINTER(AttnArgs), POINTER(c_size_t)],
         "paged_attn_decode": [c_void_p, POINTER(Layout), POINTER(AttnArgs), c_void_p],
         "paged_attn_verify": [c_void_p, POINTER(Layout), POINTER(AttnArgs), c_void_p],
@@ -204,6 +205,16 @@ def rows_put(pool: Pool, table: torch.Tensor, seq_len: torch.Tensor, k_new: torc
     _need(v_new, torch.bfloat16, "v_new", shape)
     lay = _layout(pool, table, seq_len, R, max_seq_len, ring_pages)
     _check(load().kv_rows_put(pool.handle, ctypes.byref(lay), _ptr(k_new), _ptr(v_new), _stream_handle(stream)))
+
+
+def pages_copy(pool: Pool, src_ids: torch.Tensor, dst_ids: torch.Tensor, stream=None):
+    """kv_pages_copy: page dst_ids[i] gets the contents of page src_ids[i] (device int32 [n])."""
+    _need(src_ids, torch.int32, "src_ids")
+    _need(dst_ids, torch.int32, "dst_ids", tuple(src_ids.shape))
+    if src_ids.dim() != 1:
+        raise ValueError("src_ids must be 1-D")
+    n = int(src_ids.shape[0])
+    _check(load().kv_pages_copy(pool.handle, _ptr(src_ids), _ptr(dst_ids), n, _stream_handle(stream)))
 
 
 def workspace_size(pool: Pool, table: torch.Tensor, seq_len: torch.Tensor, rows: int, q_heads: int,

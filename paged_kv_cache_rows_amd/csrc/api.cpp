@@ -336,6 +336,44 @@ kv_status kv_stream_pages(const kv_pool *pool, int32_t stream, int32_t *ids_out,
     return ok();
 }
 
+kv_status kv_pages_copy(const kv_pool *pool, const int32_t *src_ids, const int32_t *dst_ids, int32_t n,
+                        void *hip_stream) {
+    if (!pool) return fail(KV_E_ARG, "kv_pages_copy: pool is null");
+    if (n < 0) return fail(KV_E_ARG, "kv_pages_copy: n %d < 0", n);
+    if (n == 0) return ok();
+    if (!src_ids || !dst_ids) return fail(KV_E_ARG, "kv_pages_copy: src_ids or dst_ids is null");
+    hipStream_t hs = reinterpret_cast<hipStream_t>(hip_stream);
+    if (check_enabled()) {
+        std::vector<int32_t> src(n), dst(n);
+        if (hipMemcpyAsync(src.data(), src_ids, sizeof(int32_t) * n, hipMemcpyDeviceToHost, hs) != hipSuccess ||
+            hipMemcpyAsync(dst.data(), dst_ids, sizeof(int32_t) * n, hipMemcpyDeviceToHost, hs) != hipSuccess ||
+            hipStreamSynchronize(hs) != hipSuccess)
+            return fail(KV_E_DEVICE, "kv_pages_copy: KVP_CHECK copy failed");
+        std::vector<char> is_src(pool->num_pages, 0), is_dst(pool->num_pages, 0);
+        for (int i = 0; i < n; ++i) {
+            if (src[i] < 0 || src[i] >= pool->num_pages || dst[i] < 0 || dst[i] >= pool->num_pages)
+                return fail(KV_E_ARG, "kv_pages_copy: pair %d (%d -> %d) outside [0, %d)", i, src[i], dst[i],
+                            pool->num_pages);
+            if (is_dst[dst[i]]) return fail(KV_E_ARG, "kv_pages_copy: page %d is a destination twice", dst[i]);
+            is_src[src[i]] = 1;
+            is_dst[dst[i]] = 1;
+        }
+        for (int i = 0; i < n; ++i)
+            if (is_src[dst[i]]) return fail(KV_E_ARG, "kv_pages_copy: page %d is both a source and a destination", dst[i]);
+    }
+    kvp::CopyArgs ca;
+    ca.k_pages = pool->k_pages;
+    ca.v_pages = pool->v_pages;
+    ca.src = src_ids;
+    ca.dst = dst_ids;
+    ca.n = n;
+    ca.num_pages = pool->num_pages;
+    ca.page_elems = (size_t)pool->num_kv_heads * pool->page_size * pool->head_dim;
+    const hipError_t e = kvp::launch_pages_copy(ca, hs);
+    if (e != hipSuccess) return fail(KV_E_DEVICE, "kv_pages_copy: launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
 kv_status kv_rows_put(const kv_pool *pool, const kv_layout *lay, const void *k_new, const void *v_new,
                       void *hip_stream) {
     kv_status st = check_layout(pool, lay, "kv_rows_put");

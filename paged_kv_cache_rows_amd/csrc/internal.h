@@ -42,6 +42,16 @@ struct PartArgs {
     float scale_log2;  // scale * log2(e)
 };
 
+// Arguments of the page copy (kept states): page dst[i] gets page src[i], K and V.
+struct CopyArgs {
+    uint16_t *k_pages;
+    uint16_t *v_pages;
+    const int32_t *src;
+    const int32_t *dst;
+    int n, num_pages;
+    size_t page_elems;   // Hkv * P * D
+};
+
 struct MergeArgs {
     const float *ws_acc;
     const float *ws_ml;
@@ -88,5 +98,6 @@ hipError_t launch_rows_put(const RowsArgs &a, hipStream_t st);
 hipError_t launch_part_valu(int D, int G, int NQ, const PartArgs &a, int S, hipStream_t st);
 hipError_t launch_part_mfma(int D, int G, const MfmaPlan &p, const PartArgs &a, int S, hipStream_t st);
 hipError_t launch_merge(const MergeArgs &a, hipStream_t st);
+hipError_t launch_pages_copy(const CopyArgs &a, hipStream_t st);
 
 }  // namespace kvp

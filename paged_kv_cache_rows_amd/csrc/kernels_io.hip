@@ -36,6 +36,56 @@ __global__ __launch_bounds__(256) void rows_put_kernel(const RowsArgs a) {
     }
 }
 
+// Page copy (TensorFold PR #1620, opening description, Kept states bullet: a stream's state is
+// kept by copying the pages its table walks).  Block (x, y) copies the x-th run of
+// 256 * PPT 16-byte pieces of pair y, K and V, with streaming loads and stores: the bytes are
+// touched once.
+constexpr int COPY_PPT = 8;
+
+__global__ __launch_bounds__(256) void pages_copy_kernel(const CopyArgs a) {
+    const int i = blockIdx.y;
+    const int sp = a.src[i], dp = a.dst[i];
+    if ((unsigned)sp >= (unsigned)a.num_pages || (unsigned)dp >= (unsigned)a.num_pages || sp == dp) return;
+    const size_t pieces = a.page_elems / 8;
+    const u32x4 *ks = reinterpret_cast<const u32x4 *>(a.k_pages + (size_t)sp * a.page_elems);
+    const u32x4 *vs = reinterpret_cast<const u32x4 *>(a.v_pages + (size_t)sp * a.page_elems);
+    u32x4 *kd = reinterpret_cast<u32x4 *>(a.k_pages + (size_t)dp * a.page_elems);
+    u32x4 *vd = reinterpret_cast<u32x4 *>(a.v_pages + (size_t)dp * a.page_elems);
+    const size_t p0 = (size_t)blockIdx.x * (256 * COPY_PPT) + threadIdx.x;
+    u32x4 kx[COPY_PPT], vx[COPY_PPT];
+#pragma unroll
+    for (int u = 0; u < COPY_PPT; ++u) {
+        const size_t pc = min(p0 + (size_t)u * 256, pieces - 1);
+        kx[u] = __builtin_nontemporal_load(ks + pc);
+        vx[u] = __builtin_nontemporal_load(vs + pc);
+    }
+#pragma unroll
+    for (int u = 0; u < COPY_PPT; ++u) {
+        const size_t pc = p0 + (size_t)u * 256;
+        if (pc < pieces) {
+            __builtin_nontemporal_store(kx[u], kd + pc);
+            __builtin_nontemporal_store(vx[u], vd + pc);
+        }
+    }
+}
+
+hipError_t launch_pages_copy(const CopyArgs &args, hipStream_t st) {
+    if (args.n <= 0) return hipSuccess;
+    const size_t pieces = args.page_elems / 8;
+    const unsigned bx = (unsigned)((pieces + 256 * COPY_PPT - 1) / (256 * COPY_PPT));
+    // gridDim.y is limited to 65535: launch the pairs in slices
+    for (int i0 = 0; i0 < args.n; i0 += 65535) {
+        CopyArgs a = args;
+        a.src = args.src + i0;
+        a.dst = args.dst + i0;
+        a.n = min(args.n - i0, 65535);
+        hipLaunchKernelGGL(pages_copy_kernel, dim3(bx, a.n), dim3(256), 0, st, a);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
 hipError_t launch_rows_put(const RowsArgs &a, hipStream_t st) {
     const int blocks = a.S * a.R;
     if (blocks == 0) return hipSuccess;

@@ -480,3 +480,26 @@ def test_planted_tree_without_the_prefix_turns_pins_red(monkeypatch):
         return [j for j in real(length, rows, r, mask, window) if j >= length - rows]
     monkeypatch.setattr(oatt, "tree_keys", no_prefix)
     assert not _tree_pins_pass()
+
+
+# ----------------------------------------------------------------------------- kept states
+def test_copy_pages_then_gather_reads_the_same_stream():
+    rng = np.random.default_rng(11)
+    N, Hkv, P, D, L = 12, 2, 5, 3, 17
+    pages = rng.standard_normal((N, Hkv, P, D))
+    src = [7, 2, 9, 4]                          # the stream's table: ceil(17 / 5) = 4 pages
+    dst = [0, 11, 5, 8]                         # freshly leased pages for the kept state
+    before = opages.gather_linear(pages, src, L, P)
+    copied = oracle.copy_pages(pages, src, dst)
+    np.testing.assert_array_equal(opages.gather_linear(copied, dst, L, P), before)
+    # the source pages and every page outside dst are untouched
+    untouched = [i for i in range(N) if i not in dst]
+    np.testing.assert_array_equal(copied[untouched], pages[untouched])
+
+
+def test_copy_pages_reads_sources_before_any_write():
+    pages = np.arange(4 * 1 * 2 * 1, dtype=np.float64).reshape(4, 1, 2, 1)
+    out = oracle.copy_pages(pages, [0, 1], [1, 2])           # page 1 is a source and a destination
+    np.testing.assert_array_equal(out[1], pages[0])
+    np.testing.assert_array_equal(out[2], pages[1])          # the old page 1, not the copy of page 0
+    np.testing.assert_array_equal(oracle.copy_pages(pages, [0, 9], [3, 1])[1], pages[1])   # 9 outside: skipped
