@@ -161,7 +161,7 @@ kv_status make_plan(const kv_pool *pool, const kv_layout *lay, const kv_attn_arg
         p->align = vp.align;
     }
     if (p->mfma) {
-        p->n_splits = splits_for(lay->max_seq_len, p->R, a->window, p->chunk);
+        p->n_splits = p->mp.direct ? 1 : splits_for(lay->max_seq_len, p->R, a->window, p->chunk);
         p->even = false;
         p->align = 1;
     }
@@ -207,7 +207,7 @@ kv_status run_attention(const kv_pool *pool, const kv_layout *lay, const kv_attn
     pa.chunk = p.chunk;
     pa.out = static_cast<uint16_t *>(a->out);
     pa.tree = tree;
-    pa.direct = (p.mfma && p.n_splits == 1) ? 1 : 0;
+    pa.direct = (p.mfma && p.mp.direct) ? 1 : 0;
     const float scale = a->scale > 0.f ? a->scale : 1.0f / std::sqrt((float)p.D);
     pa.scale_log2 = scale * 1.4426950408889634f;
 

@@ -90,7 +90,9 @@ bool mfma_supported(int D, int G, int R);
 // the call's shape only.
 struct MfmaPlan {
     int qw, tiles, chunk;
-    int ks;   // key sub-tiles per step (2: 8-wave workgroups, D = 128 only)
+    int ks;       // key sub-tiles per step (2: 8-wave workgroups, D = 128 only)
+    bool direct;  // one split per query tile, covering exactly the keys its rows see; the bf16
+                  // output is written by the part kernel (chunk then bounds that key span)
 };
 MfmaPlan mfma_plan(int D, int G, int R, int S, int Hkv, int max_seq_len, int window);
 

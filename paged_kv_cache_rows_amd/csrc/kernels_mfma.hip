@@ -76,6 +76,7 @@ MfmaPlan mfma_plan(int D, int G, int R, int S, int Hkv, int max_seq_len, int win
     // about 280 registers, one wave per SIMD, and measured slower on every workload here
     p.qw = 1;
     p.ks = 1;
+    p.direct = false;
     p.tiles = (nq + 64 * p.qw - 1) / (64 * p.qw);
     const int kt = mfma_tile_keys(D);
     int span = max_seq_len;
@@ -86,7 +87,8 @@ MfmaPlan mfma_plan(int D, int G, int R, int S, int Hkv, int max_seq_len, int win
     // directly (partials and their merge cost far more than their bytes: a 512-row prompt
     // chunk over 2048 keys takes 53 us with 4 splits and a merge, 38 us with one)
     if (groups >= 256) {
-        p.chunk = (span + kt - 1) / kt * kt;
+        p.direct = true;
+        p.chunk = (span + kt - 1) / kt * kt;     // bounds the keys of one tile
         if (p.chunk < kt) p.chunk = kt;
         p.ks = D == 128 ? 2 : 1;     // 8 waves over two key sub-tiles: half the tile chain
         return p;
@@ -155,8 +157,12 @@ __global__ __launch_bounds__(256 * KS) void part_mfma_kernel(const PartArgs a) {
     const int r_last = (min(NQ, v0 + M) - 1) / G;
     const int p_first = L - R + r_first, p_last = L - R + r_last;
     const int lo_stream = W > 0 ? max(0, L - R - W + 1) : 0;
-    const int c0 = (lo_stream / CH + split) * CH;
     const int lo_tile = W > 0 ? max(0, p_first - W + 1) : 0;
+    // a split is a chunk of absolute positions; a direct call's one split starts at the tile's
+    // first visible key, and its chunk (>= window + R - 1, or >= max_seq_len) then covers every
+    // key the tile's rows see (the bound only matters for lengths beyond max_seq_len: it keeps
+    // the table entries the tile reads within the cached ones)
+    const int c0 = a.direct ? lo_tile : (lo_stream / CH + split) * CH;
     const int kbeg = max(c0, lo_tile);
     const int kend = min(c0 + CH, p_last + 1);
     if (kbeg >= kend) {
