@@ -73,12 +73,17 @@ def measured_traffic():
 
 
 class DecodeSetup:
-    def __init__(self, w, order_seed, torch, binding, staging, workloads, identity=False):
+    def __init__(self, w, order_seed, torch, binding, staging, workloads, identity=False, contiguous=False):
         self.w = w
         self.torch = torch
-        order = (workloads.identity_order(w.pool_pages) if identity
+        order = (workloads.identity_order(w.pool_pages) if identity or contiguous
                  else workloads.free_order(w.pool_pages, order_seed))
-        self.c = staging.make_cache(w, device="cuda", order=order)
+        if contiguous:
+            # streams that grew side by side, a page each in turn, under the contiguous policy
+            self.c = staging.make_cache(w, device="cuda", order=order, lease_policy=binding.KV_LEASE_CONTIGUOUS,
+                                        grow_in_turn=1)
+        else:
+            self.c = staging.make_cache(w, device="cuda", order=order)
         self.ks, self.vs = workloads.kv_history(w, device="cuda")
         staging.write_history(self.c, self.ks, self.vs)
         self.q = workloads.queries(w, device="cuda")
@@ -362,6 +367,7 @@ def main():
               "runs per GPU on its own streams); run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
+    import numpy as np
     import torch
 
     import oracle
@@ -434,6 +440,17 @@ def main():
         lms, lpart, _, _ = timed_steps(lin, max(20, args.steps // 4), 5, torch, binding)
         result["identity_table"] = {"us_per_layer": round(lms * 1e3, 2), "part_us_mean": round(lpart * 1e3, 2),
                                     "paged_over_identity": round(part_ms / lpart, 4)}
+        log("[bench] contiguous-lease arm")
+        cg = DecodeSetup(w, 0, torch, binding, staging, workloads, contiguous=True)
+        cms, cpart, _, _ = timed_steps(cg, max(20, args.steps // 4), 5, torch, binding)
+        runs = [1 + int((np.diff(cg.c.table_host[s][:w.pages_for(L)]) != 1).sum()) for s, L in enumerate(w.lengths)]
+        result["contiguous_leases"] = {"us_per_layer": round(cms * 1e3, 2), "part_us_mean": round(cpart * 1e3, 2),
+                                       "paged_over_contiguous": round(part_ms / cpart, 4),
+                                       "runs_per_stream": runs,
+                                       "bytes_equal": bool(torch.equal(cg.out.view(torch.int16),
+                                                                       setup.out.view(torch.int16)))}
+        del cg
+        torch.cuda.empty_cache()
         log("[bench] kept-state page copy")
         result["kept_state_copy"] = kept_state_copy(setup, torch, binding)
         same = torch.equal(lin.out.view(torch.int16), setup.out.view(torch.int16))

@@ -107,11 +107,29 @@ kv_status kv_pool_create(const kv_pool_desc *desc, kv_pool **out);
 kv_status kv_pool_destroy(kv_pool *pool);
 
 /* Lease n pages to a stream as it grows (TensorFold PR #1620, opening description: streams
- * take pages from the shared pool as their caches grow).  Pages come off the front of the free queue in queue order,
- * are appended to the stream's lease list and are written to page_ids_out (host [n]).
+ * take pages from the shared pool as their caches grow).  Which ids are handed out follows the
+ * pool's lease policy (below; by default the front of the free queue, in queue order).  They
+ * are appended to the stream's lease list and written to page_ids_out (host [n]).
  * All or nothing: with fewer than n free pages it returns KV_E_NO_PAGES and changes nothing.
  * KV_E_ARG for a bad stream id, n < 0, or a null output with n > 0.  Thread-safe per pool. */
 kv_status kv_page_lease(kv_pool *pool, int32_t stream, int32_t n, int32_t *page_ids_out);
+
+/* Lease policies.
+ * KV_LEASE_QUEUE (the default): the first n ids of the free queue, in queue order.
+ * KV_LEASE_CONTIGUOUS: keep each stream in runs of adjacent page ids while the pool has room,
+ *   and fall back to scattered pages when it does not (TensorFold PR #1620, first review: the
+ *   full layers may keep a contiguous cache until the pool needs the room).  The ids come from
+ *   the first of these steps that applies:
+ *   1. the stream holds pages, its last leased id is t, and t+1 .. t+n are all free: those;
+ *   2. the longest run of adjacent free ids that holds n (the lowest such run on a tie), say
+ *      [a, b): ids start .. start+n-1 with start = a when a == 0, else a + (b - a - n) / 2
+ *      (half the run's spare room stays behind the page before it, whose stream may grow);
+ *   3. the n lowest free ids, in increasing order.
+ * Either policy removes the ids it hands out from the free queue; releases append to its back
+ * as always.  The page table is the only thing the kernels read, so the policy changes where
+ * pages live, never a result.  KV_E_ARG for an unknown policy.  Thread-safe per pool. */
+enum { KV_LEASE_QUEUE = 0, KV_LEASE_CONTIGUOUS = 1 };
+kv_status kv_pool_set_lease_policy(kv_pool *pool, int32_t policy);
 
 /* Return all of a stream's pages to the back of the free queue, in the order they were leased
  * (released pages are handed out again by later leases, which the PR's model test covers).  KV_E_ARG for

@@ -11,9 +11,22 @@ so this library fixes one and the model states it:
   * release(stream) appends the stream's pages to the back of the queue in the order they
     were leased, and empties the stream's list.
 
+A second lease policy, "contiguous", follows the first review of the same PR (the full layers
+could keep a contiguous cache until the pool needs the room).  It hands out ids by the first
+of these that applies, and removes them from the queue wherever they sit:
+
+  1. extension: the stream holds pages, its newest is t, and t+1, ..., t+n are all free;
+  2. placement: among the maximal runs of adjacent free ids with room for n, the longest
+     (lowest on a tie), [a, b); the n ids from a if a is 0, else from a + (b - a - n) // 2,
+     which leaves half of the run's spare room to the stream that owns page a - 1;
+  3. fallback: the n smallest free ids, ascending.
+
 Pins: tests/test_oracle_pins.py checks, against brute-force bookkeeping with sets, that after
 any random sequence of leases and releases the leased lists and the free list partition
 range(N), no id is leased twice, failed leases change nothing, and hand-out follows the queue.
+The contiguous policy is pinned by a hand-worked sequence (tests/golden/contiguous_leases.json)
+that reaches each step and the tie rule, and by properties of random sequences: the same
+partition, and that every lease is one run of adjacent ids whenever the free set has one.
 """
 from collections import deque
 
@@ -30,13 +43,49 @@ class LeaseModel:
         self.num_pages = num_pages
         self.free = deque(order)
         self.leased = [[] for _ in range(max_streams)]
+        self.policy = "queue"
+
+    def set_policy(self, policy: str):
+        if policy not in ("queue", "contiguous"):
+            raise ValueError("policy is 'queue' or 'contiguous'")
+        self.policy = policy
+
+    def _free_runs(self):
+        """Maximal runs [a, b) of adjacent free ids, in increasing order of a."""
+        runs = []
+        for i in sorted(self.free):
+            if runs and runs[-1][1] == i:
+                runs[-1][1] = i + 1
+            else:
+                runs.append([i, i + 1])
+        return [tuple(r) for r in runs]
+
+    def _contiguous_ids(self, stream: int, n: int):
+        free = set(self.free)
+        mine = self.leased[stream]
+        if mine:
+            want = [mine[-1] + k for k in range(1, n + 1)]
+            if all(i in free for i in want):
+                return want
+        fits = [(a, b) for a, b in self._free_runs() if b - a >= n]
+        if fits:
+            longest = max(b - a for a, b in fits)
+            a, b = next((a, b) for a, b in fits if b - a == longest)
+            start = a if a == 0 else a + (b - a - n) // 2
+            return list(range(start, start + n))
+        return sorted(free)[:n]
 
     def lease(self, stream: int, n: int):
         if n < 0 or not (0 <= stream < len(self.leased)):
             raise ValueError("bad stream or count")
         if n > len(self.free):
             raise NoPages(f"{n} pages asked, {len(self.free)} free")
-        got = [self.free.popleft() for _ in range(n)]
+        if self.policy == "queue" or n == 0:
+            got = [self.free.popleft() for _ in range(n)]
+        else:
+            got = self._contiguous_ids(stream, n)
+            taken = set(got)
+            self.free = deque(i for i in self.free if i not in taken)
         self.leased[stream].extend(got)
         return got
 

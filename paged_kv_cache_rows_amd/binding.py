@@ -20,11 +20,12 @@ import torch
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkvpaged.so")
 
 KV_OK, KV_E_ARG, KV_E_SHAPE, KV_E_NO_PAGES, KV_E_WORKSPACE, KV_E_DEVICE = 0, -1, -2, -3, -4, -5
+KV_LEASE_QUEUE, KV_LEASE_CONTIGUOUS = 0, 1
 STATUS_NAMES = {0: "KV_OK", -1: "KV_E_ARG", -2: "KV_E_SHAPE", -3: "KV_E_NO_PAGES",
                 -4: "KV_E_WORKSPACE", -5: "KV_E_DEVICE"}
 
 # The entry points include/kvpaged.h declares (checked against the built library's exports).
-EXPORTS = ("kv_pool_create", "kv_pool_destroy", "kv_page_lease", "kv_page_release",
+EXPORTS = ("kv_pool_create", "kv_pool_destroy", "kv_page_lease", "kv_page_release", "kv_pool_set_lease_policy",
            "kv_pool_free_count", "kv_stream_pages", "kv_rows_put", "kv_pages_copy", "paged_attn_workspace_size",
            "paged_attn_decode", "paged_attn_verify", "paged_attn_verify_tree", "paged_attn_prefill",
            "kv_set_part_events",
@@ -71,6 +72,7 @@ def load(path: str = LIB_PATH):
         "kv_pool_destroy": [c_void_p],
         "kv_page_lease": [c_void_p, c_int32, c_int32, i32p],
         "kv_page_release": [c_void_p, c_int32],
+        "kv_pool_set_lease_policy": [c_void_p, c_int32],
         "kv_pool_free_count": [c_void_p, i32p],
         "kv_stream_pages": [c_void_p, c_int32, i32p, c_int32, i32p],
         "kv_rows_put": [c_void_p, POINTER(Layout), c_void_p, c_void_p, c_void_p],
@@ -158,6 +160,10 @@ class Pool:
         ids = (c_int32 * max(n, 1))()
         _check(load().kv_page_lease(self.handle, stream, n, ids))
         return [int(ids[i]) for i in range(n)]
+
+    def set_lease_policy(self, policy: int):
+        """KV_LEASE_QUEUE (default) or KV_LEASE_CONTIGUOUS: which free ids later leases take."""
+        _check(load().kv_pool_set_lease_policy(self.handle, policy))
 
     def release(self, stream: int):
         _check(load().kv_page_release(self.handle, stream))

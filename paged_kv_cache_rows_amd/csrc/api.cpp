@@ -5,6 +5,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -21,6 +22,8 @@ struct kv_pool {
     uint16_t *v_pages;
     mutable std::mutex mu;
     std::deque<int32_t> free_q;
+    std::vector<char> is_free;       // is_free[id]: id is in free_q
+    int32_t policy = KV_LEASE_QUEUE;
     std::vector<std::vector<int32_t>> leased;
 };
 
@@ -240,6 +243,47 @@ kv_status run_attention(const kv_pool *pool, const kv_layout *lay, const kv_attn
     return ok();
 }
 
+// The ids KV_LEASE_CONTIGUOUS hands out for a lease of n (1 <= n <= free count) to a stream
+// holding `held`: its own run extended, else a place in the longest free run that fits, else
+// the lowest free ids.
+std::vector<int32_t> contiguous_pick(const kv_pool *pool, const std::vector<int32_t> &held, int32_t n) {
+    const int32_t N = pool->num_pages;
+    const auto &fr = pool->is_free;
+    std::vector<int32_t> got;
+    got.reserve(n);
+    if (!held.empty()) {
+        const int64_t t = held.back();
+        bool room = t + n < N;
+        for (int64_t i = t + 1; room && i <= t + n; ++i) room = fr[i] != 0;
+        if (room) {
+            for (int32_t i = 1; i <= n; ++i) got.push_back((int32_t)(t + i));
+            return got;
+        }
+    }
+    int32_t best_a = -1, best_len = 0;
+    for (int32_t a = 0; a < N;) {
+        if (!fr[a]) {
+            ++a;
+            continue;
+        }
+        int32_t b = a;
+        while (b < N && fr[b]) ++b;
+        if (b - a >= n && b - a > best_len) {
+            best_a = a;
+            best_len = b - a;
+        }
+        a = b;
+    }
+    if (best_a >= 0) {
+        const int32_t start = best_a == 0 ? 0 : best_a + (best_len - n) / 2;
+        for (int32_t i = 0; i < n; ++i) got.push_back(start + i);
+        return got;
+    }
+    for (int32_t id = 0; id < N && (int32_t)got.size() < n; ++id)
+        if (fr[id]) got.push_back(id);
+    return got;
+}
+
 }  // namespace
 
 extern "C" {
@@ -277,6 +321,7 @@ kv_status kv_pool_create(const kv_pool_desc *d, kv_pool **out) {
     p->k_pages = static_cast<uint16_t *>(d->k_pages);
     p->v_pages = static_cast<uint16_t *>(d->v_pages);
     p->free_q.assign(order.begin(), order.end());
+    p->is_free.assign(d->num_pages, 1);
     p->leased.assign(d->max_streams, {});
     *out = p;
     return ok();
@@ -297,11 +342,33 @@ kv_status kv_page_lease(kv_pool *pool, int32_t stream, int32_t n, int32_t *ids) 
     if ((size_t)n > pool->free_q.size())
         return fail(KV_E_NO_PAGES, "kv_page_lease: %d pages asked, %zu free", n, pool->free_q.size());
     auto &lst = pool->leased[stream];
-    for (int i = 0; i < n; ++i) {
-        ids[i] = pool->free_q.front();
-        pool->free_q.pop_front();
-        lst.push_back(ids[i]);
+    if (n == 0) return ok();
+    if (pool->policy == KV_LEASE_QUEUE) {
+        for (int i = 0; i < n; ++i) {
+            ids[i] = pool->free_q.front();
+            pool->free_q.pop_front();
+            pool->is_free[ids[i]] = 0;
+            lst.push_back(ids[i]);
+        }
+        return ok();
     }
+    const std::vector<int32_t> got = contiguous_pick(pool, lst, n);
+    for (int i = 0; i < n; ++i) {
+        ids[i] = got[i];
+        pool->is_free[got[i]] = 0;
+        lst.push_back(got[i]);
+    }
+    auto &q = pool->free_q;
+    q.erase(std::remove_if(q.begin(), q.end(), [&](int32_t id) { return !pool->is_free[id]; }), q.end());
+    return ok();
+}
+
+kv_status kv_pool_set_lease_policy(kv_pool *pool, int32_t policy) {
+    if (!pool) return fail(KV_E_ARG, "kv_pool_set_lease_policy: pool is null");
+    if (policy != KV_LEASE_QUEUE && policy != KV_LEASE_CONTIGUOUS)
+        return fail(KV_E_ARG, "kv_pool_set_lease_policy: unknown policy %d", policy);
+    std::lock_guard<std::mutex> lk(pool->mu);
+    pool->policy = policy;
     return ok();
 }
 
@@ -311,7 +378,10 @@ kv_status kv_page_release(kv_pool *pool, int32_t stream) {
     if (stream < 0 || stream >= pool->max_streams)
         return fail(KV_E_ARG, "kv_page_release: stream %d outside [0, %d)", stream, pool->max_streams);
     auto &lst = pool->leased[stream];
-    for (int32_t id : lst) pool->free_q.push_back(id);
+    for (int32_t id : lst) {
+        pool->free_q.push_back(id);
+        pool->is_free[id] = 1;
+    }
     lst.clear();
     return ok();
 }

@@ -33,15 +33,27 @@ class Cache:
 
 
 def make_cache(w: Workload, device="cuda", order=None, fill_bits: int = NAN_BITS,
-               lengths=None) -> Cache:
+               lengths=None, lease_policy: int | None = None, grow_in_turn: int = 0) -> Cache:
+    """`lease_policy`: set on the pool before any lease (KV_LEASE_QUEUE by default).
+    `grow_in_turn` > 0: the streams lease their pages in turns of that many pages each, as
+    streams that grow side by side do; 0: each stream leases all its pages at once."""
     lengths = list(w.lengths if lengths is None else lengths)
     pool = binding.Pool(w.pool_pages, w.page_size, w.kv_heads, w.head_dim, max_streams=w.streams,
                         device=device, free_order=order, fill_bits=fill_bits)
+    if lease_policy is not None:
+        pool.set_lease_policy(lease_policy)
     stride = w.table_stride
     table = np.full((w.streams, stride), -1, dtype=np.int32)
-    for s, L in enumerate(lengths):
-        ids = pool.lease(s, w.pages_for(L))
-        table[s, :len(ids)] = ids
+    need = [w.pages_for(L) for L in lengths]
+    have = [0] * len(lengths)
+    turn = grow_in_turn if grow_in_turn > 0 else max(need + [1])
+    while any(h < n for h, n in zip(have, need)):
+        for s in range(len(lengths)):
+            k = min(turn, need[s] - have[s])
+            if k > 0:
+                ids = pool.lease(s, k)
+                table[s, have[s]:have[s] + k] = ids
+                have[s] += k
     table_d = torch.from_numpy(table).to(device)
     seq = torch.tensor(lengths, dtype=torch.int32, device=device)
     return Cache(w, pool, table_d, table, seq, lengths, max(lengths), w.ring_pages)

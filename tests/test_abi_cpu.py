@@ -117,8 +117,9 @@ def test_lease_is_all_or_nothing(lib):
     lib.kv_pool_destroy(h)
 
 
-@pytest.mark.parametrize("seed", range(5))
+@pytest.mark.parametrize("seed", range(8))
 def test_leases_match_the_oracle_model(lib, seed):
+    # seeds 0..3: the queue policy throughout; 4..7: the policy switches at random
     rng = random.Random(seed)
     N, S = 60, 6
     order = list(range(N))
@@ -129,6 +130,11 @@ def test_leases_match_the_oracle_model(lib, seed):
     buf = (ctypes.c_int32 * N)()
     for _ in range(300):
         s = rng.randrange(S)
+        if seed >= 4 and rng.random() < 0.05:
+            pol = rng.choice(["queue", "contiguous"])
+            assert lib.kv_pool_set_lease_policy(
+                h, binding.KV_LEASE_CONTIGUOUS if pol == "contiguous" else binding.KV_LEASE_QUEUE) == 0
+            model.set_policy(pol)
         if rng.random() < 0.65:
             n = rng.randrange(0, 15)
             st = lib.kv_page_lease(h, s, n, buf)
@@ -229,4 +235,34 @@ def test_verify_tree_refuses_before_launch(lib):
     assert f(h, ctypes.byref(_layout(R=9)), ctypes.byref(_args()), 0x80000, None) == binding.KV_E_ARG  # R > 8
     assert f(h, ctypes.byref(_layout(R=4)), ctypes.byref(_args(Hq=12)), 0x80000, None) == binding.KV_E_SHAPE
     assert lib.kv_last_error()
+    lib.kv_pool_destroy(h)
+
+
+def test_library_follows_the_hand_worked_contiguous_sequence(lib):
+    import json
+    fx = json.load(open(os.path.join(ROOT, "tests", "golden", "contiguous_leases.json")))
+    st, h, _ = _create(lib, num_pages=fx["num_pages"], streams=fx["max_streams"])
+    assert st == 0
+    buf = (ctypes.c_int32 * fx["num_pages"])()
+    pol = {"queue": binding.KV_LEASE_QUEUE, "contiguous": binding.KV_LEASE_CONTIGUOUS}
+    for step in fx["steps"]:
+        if step["op"] == "policy":
+            assert lib.kv_pool_set_lease_policy(h, pol[step["policy"]]) == 0
+        elif step["op"] == "release":
+            assert lib.kv_page_release(h, step["stream"]) == 0
+        else:
+            r = lib.kv_page_lease(h, step["stream"], step["n"], buf)
+            if step["expect"] == "no_pages":
+                assert r == binding.KV_E_NO_PAGES
+            else:
+                assert r == 0 and list(buf[:step["n"]]) == step["expect"], step
+        if "free_after" in step:
+            cnt = ctypes.c_int32()
+            lib.kv_pool_free_count(h, ctypes.byref(cnt))
+            assert cnt.value == len(step["free_after"])
+    for s, want in enumerate(fx["final_leased"]):
+        n = ctypes.c_int32()
+        assert lib.kv_stream_pages(h, s, buf, fx["num_pages"], ctypes.byref(n)) == 0
+        assert list(buf[:n.value]) == want
+    assert lib.kv_pool_set_lease_policy(h, 7) == binding.KV_E_ARG
     lib.kv_pool_destroy(h)

@@ -503,3 +503,121 @@ def test_copy_pages_reads_sources_before_any_write():
     np.testing.assert_array_equal(out[1], pages[0])
     np.testing.assert_array_equal(out[2], pages[1])          # the old page 1, not the copy of page 0
     np.testing.assert_array_equal(oracle.copy_pages(pages, [0, 9], [3, 1])[1], pages[1])   # 9 outside: skipped
+
+
+# ----------------------------------------------------------------------------- contiguous leases
+def _run_lease_golden(model_cls=None):
+    """Drive a lease model through the hand-worked sequence of tests/golden/contiguous_leases.json
+    (TensorFold PR #1620, first review: keep the full layers contiguous until the pool needs
+    the room); AssertionError on the first difference."""
+    fx = json.load(open(os.path.join(os.path.dirname(GOLDEN), "contiguous_leases.json")))
+    m = (model_cls or oracle.LeaseModel)(fx["num_pages"], fx["max_streams"])
+    for st in fx["steps"]:
+        if st["op"] == "policy":
+            m.set_policy(st["policy"])
+            continue
+        if st["op"] == "release":
+            m.release(st["stream"])
+        else:
+            try:
+                got = m.lease(st["stream"], st["n"])
+            except oracle.NoPages:
+                got = "no_pages"
+            assert got == st["expect"], (st, got)
+        if "free_after" in st:
+            assert list(m.free) == st["free_after"], (st, list(m.free))
+    assert m.leased == fx["final_leased"]
+
+
+def test_contiguous_leases_follow_the_hand_worked_sequence():
+    _run_lease_golden()
+
+
+def _has_run(free, n):
+    free = set(free)
+    return any(all(a + k in free for k in range(n)) for a in free)
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_contiguous_leases_keep_runs_while_the_pool_has_them(seed):
+    rng = random.Random(100 + seed)
+    N, S = 64, 6
+    m = oracle.LeaseModel(N, S)
+    m.set_policy("contiguous")
+    for _ in range(500):
+        s = rng.randrange(S)
+        if rng.random() < 0.75:
+            n = rng.randrange(1, 6)
+            free_before = set(m.free)
+            newest = m.leased[s][-1] if m.leased[s] else None
+            try:
+                got = m.lease(s, n)
+            except oracle.NoPages:
+                assert n > len(free_before)
+                continue
+            assert set(got) <= free_before and len(set(got)) == n
+            ext = None if newest is None else list(range(newest + 1, newest + n + 1))
+            if ext is not None and set(ext) <= free_before:
+                assert got == ext                                   # the stream's own run grows
+            elif _has_run(free_before, n):
+                assert got == list(range(got[0], got[0] + n))       # still one run of adjacent ids
+            else:
+                assert got == sorted(free_before)[:n]
+        else:
+            m.release(s)
+        leased = [p for lst in m.leased for p in lst]
+        assert len(set(leased)) == len(leased)
+        assert sorted(leased + list(m.free)) == list(range(N))
+
+
+def test_interleaved_growth_in_an_empty_pool_stays_in_few_runs():
+    # 4 streams grow one page at a time in turn until each holds 12 of 64 pages: the
+    # placements leave each stream room behind it, so every table is a single run
+    m = oracle.LeaseModel(64, 4)
+    m.set_policy("contiguous")
+    for _ in range(12):
+        for s in range(4):
+            m.lease(s, 1)
+    for lst in m.leased:
+        assert lst == list(range(lst[0], lst[0] + 12))
+
+
+class _StartAtRunStart(oracle.LeaseModel):
+    def _contiguous_ids(self, stream, n):
+        mine = self.leased[stream]
+        free = set(self.free)
+        if mine and all(mine[-1] + k in free for k in range(1, n + 1)):
+            return [mine[-1] + k for k in range(1, n + 1)]
+        for a, b in sorted(self._free_runs(), key=lambda r: (-(r[1] - r[0]), r[0])):
+            if b - a >= n:
+                return list(range(a, a + n))
+        return sorted(free)[:n]
+
+
+class _TieToHighest(oracle.LeaseModel):
+    def _free_runs(self):
+        return list(reversed(super()._free_runs()))
+
+
+class _FallbackInQueueOrder(oracle.LeaseModel):
+    def _contiguous_ids(self, stream, n):
+        got = super()._contiguous_ids(stream, n)
+        if got == sorted(set(self.free))[:n] and not _has_run(self.free, n):
+            return list(self.free)[:n]
+        return got
+
+
+class _NoExtension(oracle.LeaseModel):
+    def _contiguous_ids(self, stream, n):
+        saved = self.leased[stream]
+        self.leased[stream] = []
+        try:
+            return super()._contiguous_ids(stream, n)
+        finally:
+            self.leased[stream] = saved
+
+
+@pytest.mark.parametrize("cls", [_StartAtRunStart, _TieToHighest, _FallbackInQueueOrder, _NoExtension])
+def test_planted_lease_mistakes_turn_the_golden_sequence_red(cls):
+    with pytest.raises(AssertionError):
+        _run_lease_golden(cls)
