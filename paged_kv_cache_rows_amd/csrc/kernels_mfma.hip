@@ -96,7 +96,14 @@ MfmaPlan mfma_plan(int D, int G, int R, int S, int Hkv, int max_seq_len, int win
     // aim at 2 (verify windows, bound by HBM) or 4 (prompt chunks, whose causal triangle
     // leaves part of the grid idle) workgroups per CU over the whole call: long enough chunks
     // to amortise the per-workgroup set-up, short enough to keep every CU busy
-    const int64_t target = nq >= 256 ? 1024 : 512;
+    int64_t target = nq >= 256 ? 1024 : 512;
+    if (D == 128) {
+        // 8-wave workgroups over two key sub-tiles: half the workgroups for the same waves,
+        // so half the partials for the merge to read (verify window: 35.6 -> 34.9 us for the
+        // part kernel, and a merge over 8 splits instead of 16)
+        p.ks = 2;
+        target /= 2;
+    }
     int64_t chunk = ((int64_t)span * groups + target - 1) / target;
     chunk = (chunk + kt - 1) / kt * kt;
     const int lo = 4 * kt, hi = 64 * kt;
