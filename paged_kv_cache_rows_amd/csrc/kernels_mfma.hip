@@ -136,8 +136,11 @@ __global__ __launch_bounds__(256 * KS) void part_mfma_kernel(const PartArgs a) {
     constexpr int NTH = 256 * KS;    // threads
     static_assert(KS == 1 || (KS == 2 && D == 128), "key sub-tiles: 1, or 2 at D = 128");
 
-    __shared__ __attribute__((aligned(16))) uint16_t k_lds_all[KS][KT * KRS];
-    __shared__ __attribute__((aligned(16))) uint2 vt_lds_all[KS][D * KT / 4];
+    // NBUF tile buffers: with two, a step stages the next step's tiles into one buffer while it
+    // computes on the other (one barrier per step); one buffer stages and computes in turn
+    constexpr int NBUF = KS == 2 ? 2 : 1;
+    __shared__ __attribute__((aligned(16))) uint16_t k_lds_all[NBUF][KS][KT * KRS];
+    __shared__ __attribute__((aligned(16))) uint2 vt_lds_all[NBUF][KS][D * KT / 4];
     __shared__ int32_t t_lds[TC];
 
     const int tid = threadIdx.x;
@@ -236,10 +239,11 @@ __global__ __launch_bounds__(256 * KS) void part_mfma_kernel(const PartArgs a) {
     const size_t head_off = (size_t)kvh * P * D;
     // this thread's pieces: keys KPT kq .. KPT kq + KPT - 1 of sub-tile ksub, channels 8 kc .. + 8
     const int kc = (tid & 255) % CB, kq = (tid & 255) / CB;
-    uint16_t *const k_st = k_lds_all[ksub];   // staged by this thread
-    uint2 *const vt_st = vt_lds_all[ksub];
-    const uint16_t *const k_lds = k_lds_all[ksub];   // computed on by this wave
-    const uint2 *const vt_lds = vt_lds_all[ksub];
+    // buffer `buf` of the sub-tile this thread stages (ksub: thread tid stages sub-tile tid / 256,
+    // which is also the sub-tile its wave computes)
+    constexpr int KBUF = KS * KT * KRS, VBUF = KS * D * KT / 4;
+    uint16_t *const k_st0 = k_lds_all[0][ksub];
+    uint2 *const vt_st0 = vt_lds_all[0][ksub];
     u32x4 kreg0[KPT], vreg0[KPT], kreg1[KPT], vreg1[KPT];
     auto load_tile = [&](int tb, u32x4 (&kreg)[KPT], u32x4 (&vreg)[KPT]) {
         if (MODE == 0) {
@@ -298,10 +302,11 @@ __global__ __launch_bounds__(256 * KS) void part_mfma_kernel(const PartArgs a) {
     constexpr int NPF = D == 128 ? 2 : 1;
     const int kt_last = kt_first + (nt - 1) * KT;
     const int nsteps = (nt + KS - 1) / KS;
-    auto step = [&](int it, u32x4 (&kreg)[KPT], u32x4 (&vreg)[KPT]) {
+    // stage step it's sub-tile of this thread from (kreg, vreg) into buffer buf
+    auto stage = [&](int it, const u32x4 (&kreg)[KPT], const u32x4 (&vreg)[KPT], int buf) {
         const int ts = kt_first + (it * KS + (tid >> 8)) * KT;    // sub-tile this thread stages
-        const int tb = kt_first + (it * KS + ksub) * KT;          // sub-tile this wave computes
-        lds_fence();
+        uint16_t *const k_st = k_st0 + buf * KBUF;
+        uint2 *const vt_st = vt_st0 + buf * VBUF;
         // stage: K rows as loaded; V transposed into 4-key units, keys outside [kbeg, kend)
         // zeroed (they may be unused slots holding NaN)
 #pragma unroll
@@ -331,9 +336,13 @@ __global__ __launch_bounds__(256 * KS) void part_mfma_kernel(const PartArgs a) {
                 vt_st[vt_unit<D>(8 * kc + 2 * i + 1, kg)] = od;
             }
         }
-        load_tile(min(ts + NPF * KS * KT, kt_last), kreg, vreg);
-        lds_fence();
-
+    };
+    auto ts_of = [&](int it) { return kt_first + (it * KS + (tid >> 8)) * KT; };
+    // compute step it's sub-tile of this wave from buffer buf
+    auto compute = [&](int it, int buf) {
+        const int tb = kt_first + (it * KS + ksub) * KT;          // sub-tile this wave computes
+        const uint16_t *const k_lds = k_st0 + buf * KBUF;
+        const uint2 *const vt_lds = vt_st0 + buf * VBUF;
         // S^T for this wave's query columns; each K fragment feeds QW MFMAs
         f32x4_t sacc[QW][NB];
 #pragma unroll
@@ -422,13 +431,40 @@ __global__ __launch_bounds__(256 * KS) void part_mfma_kernel(const PartArgs a) {
             }
         }
     };
-    const int ts0 = kt_first + (tid >> 8) * KT;
-    load_tile(min(ts0, kt_last), kreg0, vreg0);
-    if (NPF == 2) {
+    // loads for step it + NPF go into the registers step it was staged from
+    auto step = [&](int it, u32x4 (&kreg)[KPT], u32x4 (&vreg)[KPT]) {
+        lds_fence();
+        stage(it, kreg, vreg, 0);
+        load_tile(min(ts_of(it + NPF), kt_last), kreg, vreg);
+        lds_fence();
+        compute(it, 0);
+    };
+    load_tile(min(ts_of(0), kt_last), kreg0, vreg0);
+    if constexpr (NBUF == 2) {
+        static_assert(NPF == 2, "two tile buffers go with two register sets");
+        // register set r holds steps of parity r; step it + 1 is staged into the other buffer
+        // while step it is computed, and the registers it came from take step it + 3.  The
+        // first loads keep their issue order, so every wait is for the older set only.
+        asm volatile("" ::: "memory");
+        load_tile(min(ts_of(1), kt_last), kreg1, vreg1);
+        stage(0, kreg0, vreg0, 0);
+        load_tile(min(ts_of(2), kt_last), kreg0, vreg0);
+        lds_fence();
+        for (int it = 0; it < nsteps; it += 2) {
+            stage(it + 1, kreg1, vreg1, 1);
+            load_tile(min(ts_of(it + 3), kt_last), kreg1, vreg1);
+            compute(it, 0);
+            lds_fence();
+            stage(it + 2, kreg0, vreg0, 0);
+            load_tile(min(ts_of(it + 4), kt_last), kreg0, vreg0);
+            compute(it + 1, 1);
+            lds_fence();
+        }
+    } else if (NPF == 2) {
         // keep the two first steps in issue order: the wait counts at the top of the loop
         // assume buffer 0's loads are older than buffer 1's on every path into it
         asm volatile("" ::: "memory");
-        load_tile(min(ts0 + KS * KT, kt_last), kreg1, vreg1);
+        load_tile(min(ts_of(1), kt_last), kreg1, vreg1);
         for (int it = 0; it < nsteps; it += 2) {
             step(it, kreg0, vreg0);
             step(it + 1, kreg1, vreg1);
@@ -443,7 +479,7 @@ __global__ __launch_bounds__(256 * KS) void part_mfma_kernel(const PartArgs a) {
         // waves 0..3 go on
         constexpr int NF = 4 * NCB + 2;
         static_assert(NF * 256 * 4 <= KS * KT * KRS * 2, "exchange fits the K tiles");
-        float *xch = reinterpret_cast<float *>(&k_lds_all[0][0]);
+        float *xch = reinterpret_cast<float *>(&k_lds_all[0][0][0]);
         const int xi = 64 * wave + lane;
         lds_fence();
         if (ksub == 1) {
