@@ -145,8 +145,10 @@ __global__ __launch_bounds__(256 * KS) void part_mfma_kernel(const PartArgs a) {
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = (tid >> 6) & 3;          // column wave: query vectors 16 (wave QW + b) + col
-    const int ksub = tid >> 8;                // key sub-tile this wave computes (and thread stages)
+    // wave-uniform by construction; readfirstlane tells the compiler, so that tests on them
+    // (a sub-tile inside the split, a full tile) become scalar branches, not exec-mask ones
+    const int wave = __builtin_amdgcn_readfirstlane((tid >> 6) & 3);   // column wave: query vectors 16 (wave QW + b) + col
+    const int ksub = __builtin_amdgcn_readfirstlane(tid >> 8);         // key sub-tile this wave computes (and thread stages)
     const int col = lane & 15, grp = lane >> 4;
     // work item: the dispatcher hands workgroups to the 8 XCDs round-robin (dispatch id
     // d goes to XCD d mod 8), so XCD x gets the contiguous items [x per, (x + 1) per), ordered
@@ -304,7 +306,7 @@ __global__ __launch_bounds__(256 * KS) void part_mfma_kernel(const PartArgs a) {
     const int nsteps = (nt + KS - 1) / KS;
     // stage step it's sub-tile of this thread from (kreg, vreg) into buffer buf
     auto stage = [&](int it, const u32x4 (&kreg)[KPT], const u32x4 (&vreg)[KPT], int buf) {
-        const int ts = kt_first + (it * KS + (tid >> 8)) * KT;    // sub-tile this thread stages
+        const int ts = kt_first + (it * KS + ksub) * KT;          // sub-tile this thread stages
         uint16_t *const k_st = k_st0 + buf * KBUF;
         uint2 *const vt_st = vt_st0 + buf * VBUF;
         // stage: K rows as loaded; V transposed into 4-key units, keys outside [kbeg, kend)
@@ -337,7 +339,7 @@ __global__ __launch_bounds__(256 * KS) void part_mfma_kernel(const PartArgs a) {
             }
         }
     };
-    auto ts_of = [&](int it) { return kt_first + (it * KS + (tid >> 8)) * KT; };
+    auto ts_of = [&](int it) { return kt_first + (it * KS + ksub) * KT; };
     // compute step it's sub-tile of this wave from buffer buf
     auto compute = [&](int it, int buf) {
         const int tb = kt_first + (it * KS + ksub) * KT;          // sub-tile this wave computes
