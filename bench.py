@@ -435,17 +435,29 @@ def main():
     if not args.quick:
         log("[bench] cold-cache calls (1 GiB flush before each)")
         result["cold_attention_us"] = round(cold_calls(setup, 20, torch) * 1e3, 2)
-        log("[bench] identity-table (linear) arm")
+        # the page layouts are timed in interleaved rounds, so that a drift of the clock over
+        # the run falls on every arm alike
+        log("[bench] page layouts: shuffled, identity table, contiguous leases (interleaved)")
         lin = DecodeSetup(w, 0, torch, binding, staging, workloads, identity=True)
-        lms, lpart, _, _ = timed_steps(lin, max(20, args.steps // 4), 5, torch, binding)
-        result["identity_table"] = {"us_per_layer": round(lms * 1e3, 2), "part_us_mean": round(lpart * 1e3, 2),
-                                    "paged_over_identity": round(part_ms / lpart, 4)}
-        log("[bench] contiguous-lease arm")
         cg = DecodeSetup(w, 0, torch, binding, staging, workloads, contiguous=True)
-        cms, cpart, _, _ = timed_steps(cg, max(20, args.steps // 4), 5, torch, binding)
+        arms = {"shuffled": setup, "identity": lin, "contiguous": cg}
+        parts = {k: [] for k in arms}
+        stepms = {k: [] for k in arms}
+        for _ in range(4):
+            for name, st in arms.items():
+                sms, pms, _, _ = timed_steps(st, 25, 3, torch, binding)
+                parts[name].append(pms)
+                stepms[name].append(sms)
+        med = lambda xs: sorted(xs)[len(xs) // 2]
         runs = [1 + int((np.diff(cg.c.table_host[s][:w.pages_for(L)]) != 1).sum()) for s, L in enumerate(w.lengths)]
-        result["contiguous_leases"] = {"us_per_layer": round(cms * 1e3, 2), "part_us_mean": round(cpart * 1e3, 2),
-                                       "paged_over_contiguous": round(part_ms / cpart, 4),
+        result["identity_table"] = {"us_per_layer": round(med(stepms["identity"]) * 1e3, 2),
+                                    "part_us_median": round(med(parts["identity"]) * 1e3, 2),
+                                    "shuffled_part_us_median": round(med(parts["shuffled"]) * 1e3, 2),
+                                    "paged_over_identity": round(med(parts["shuffled"]) / med(parts["identity"]), 4),
+                                    "rounds": "4 interleaved rounds of 25 steps per arm"}
+        result["contiguous_leases"] = {"us_per_layer": round(med(stepms["contiguous"]) * 1e3, 2),
+                                       "part_us_median": round(med(parts["contiguous"]) * 1e3, 2),
+                                       "paged_over_contiguous": round(med(parts["shuffled"]) / med(parts["contiguous"]), 4),
                                        "runs_per_stream": runs,
                                        "bytes_equal": bool(torch.equal(cg.out.view(torch.int16),
                                                                        setup.out.view(torch.int16)))}
