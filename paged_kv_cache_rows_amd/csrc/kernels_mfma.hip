@@ -343,6 +343,7 @@ __global__ __launch_bounds__(256 * KS) void part_mfma_kernel(const PartArgs a) {
     // compute step it's sub-tile of this wave from buffer buf
     auto compute = [&](int it, int buf) {
         const int tb = kt_first + (it * KS + ksub) * KT;          // sub-tile this wave computes
+        if (tb >= kend) return;          // a padded step past the split: nothing to add
         const uint16_t *const k_lds = k_st0 + buf * KBUF;
         const uint2 *const vt_lds = vt_st0 + buf * VBUF;
         // S^T for this wave's query columns; each K fragment feeds QW MFMAs
