@@ -93,14 +93,19 @@ hipError_t launch_rows_put(const RowsArgs &a, hipStream_t st) {
     return hipGetLastError();
 }
 
-// One wave per (stream, row, query head).  Lane = (split group sg, channel block cb): it owns
-// channels [8 cb, 8 cb + 8) of the splits i = sg, sg + SG, ...; the split groups are summed at
-// the end in a fixed order, so the result depends only on the partials, not on timing.
+// One wave per (stream, row, query head) and slice of up to 128 channels (D / 128 waves at
+// D = 512, so that no lane walks every split alone).  Lane = (split group sg, channel block cb):
+// it owns channels [8 cb, 8 cb + 8) of its slice for the splits i = sg, sg + SG, ...; the split
+// groups are summed at the end in a fixed order, so the result depends only on the partials,
+// not on timing.
 template <int D>
 __global__ __launch_bounds__(64) void merge_kernel(const MergeArgs a) {
-    constexpr int CB = D / 8;          // channel blocks of 8
-    constexpr int SG = 64 / CB;        // split groups
-    const int vec = blockIdx.x;        // (s * R + r) * Hq + h
+    constexpr int CW = D > 128 ? 128 : D;   // channels per wave
+    constexpr int NCW = D / CW;             // waves per (stream, row, query head)
+    constexpr int CB = CW / 8;              // channel blocks of 8
+    constexpr int SG = 64 / CB;             // split groups
+    const int vec = blockIdx.x / NCW;       // (s * R + r) * Hq + h
+    const int cw = blockIdx.x % NCW;        // channel slice
     const int s = vec / (a.R * a.Hq);
     const int r = (vec / a.Hq) % a.R;
     const int L = a.seq_len[s];
@@ -128,7 +133,7 @@ __global__ __launch_bounds__(64) void merge_kernel(const MergeArgs a) {
             n = min(pos / a.chunk - first + 1, a.n_splits);
         }
         const float2 *ml = reinterpret_cast<const float2 *>(a.ws_ml) + (size_t)vec * a.n_splits;
-        const float *acc = a.ws_acc + (size_t)vec * a.n_splits * D + cb * 8;
+        const float *acc = a.ws_acc + (size_t)vec * a.n_splits * D + cw * CW + cb * 8;
         for (int i = i_begin + lane; i < n; i += 64) M = fmaxf(M, ml[i].x);
         M = wave_max(M);
         if (M != -INFINITY) {
@@ -173,7 +178,7 @@ __global__ __launch_bounds__(64) void merge_kernel(const MergeArgs a) {
         uint32_t o[4];
 #pragma unroll
         for (int c = 0; c < 4; ++c) o[c] = pack_bf16x2(num[2 * c] * inv, num[2 * c + 1] * inv);
-        *reinterpret_cast<uint4 *>(a.out + (size_t)vec * D + cb * 8) = make_uint4(o[0], o[1], o[2], o[3]);
+        *reinterpret_cast<uint4 *>(a.out + (size_t)vec * D + cw * CW + cb * 8) = make_uint4(o[0], o[1], o[2], o[3]);
     }
 }
 
@@ -182,7 +187,7 @@ hipError_t launch_merge(const MergeArgs &a, hipStream_t st) {
     if (blocks == 0) return hipSuccess;
     switch (a.D) {
         case 128: hipLaunchKernelGGL(merge_kernel<128>, dim3(blocks), dim3(64), 0, st, a); break;
-        case 512: hipLaunchKernelGGL(merge_kernel<512>, dim3(blocks), dim3(64), 0, st, a); break;
+        case 512: hipLaunchKernelGGL(merge_kernel<512>, dim3(blocks * 4), dim3(64), 0, st, a); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
