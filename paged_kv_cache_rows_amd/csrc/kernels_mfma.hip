@@ -53,6 +53,15 @@ static_assert(MfmaGeom<128>::KPT == 4 && MfmaGeom<512>::KPT == 8, "thread tiling
 // (lanes: 16 channels x 4 key groups) each hit every bank pair exactly twice.
 __host__ __device__ constexpr int vt_swz(int sr) { return (((sr ^ (sr >> 3)) & 7) << 2) ^ ((sr >> 1) & 3); }
 
+// At D = 128, V^T is kept as 16-byte pair units instead: unit (ch, pp), pp = 4 pm + g, holds
+// the keys 4 kg .. 4 kg + 3 and 4 kg + 16 .. 4 kg + 19 of channel ch with kg = 8 pm + g, which
+// are exactly the 8 values of one lane's A operand in O^T = V^T P^T (key order of the C layout
+// of S^T), so one 16-byte read feeds one MFMA.  The XOR of the unit index with bits of the
+// channel spreads both the operand reads (16 channels x 4 pairs per instruction) and the
+// 8-byte half-unit stores of the staging over the banks (measured with an LDS probe: 4.3
+// cycles per 16-byte read, 8.1 per 8-byte store, against 16 and 64 without the XOR).
+__device__ __forceinline__ int vt_pair(int ch, int pp) { return ch * 8 + (pp ^ ((ch >> 1) & 7) ^ ((ch >> 4) & 7)); }
+
 template <int D>
 __device__ __forceinline__ int vt_unit(int ch, int kg) {
     using Geo = MfmaGeom<D>;
@@ -336,8 +345,15 @@ __global__ __launch_bounds__(256 * KS) void part_mfma_kernel(const PartArgs a) {
                                             __builtin_amdgcn_perm(x[3][i], x[2][i], 0x05040100u));
                 const uint2 od = make_uint2(__builtin_amdgcn_perm(x[1][i], x[0][i], 0x07060302u),
                                             __builtin_amdgcn_perm(x[3][i], x[2][i], 0x07060302u));
-                vt_st[vt_unit<D>(8 * kc + 2 * i, kg)] = ev;
-                vt_st[vt_unit<D>(8 * kc + 2 * i + 1, kg)] = od;
+                if constexpr (D == 128) {
+                    // half hh = bit 2 of kg of pair 4 (kg >> 3) + (kg & 3)
+                    const int pp = 4 * (kg >> 3) + (kg & 3), hh = (kg >> 2) & 1;
+                    vt_st[2 * vt_pair(8 * kc + 2 * i, pp) + hh] = ev;
+                    vt_st[2 * vt_pair(8 * kc + 2 * i + 1, pp) + hh] = od;
+                } else {
+                    vt_st[vt_unit<D>(8 * kc + 2 * i, kg)] = ev;
+                    vt_st[vt_unit<D>(8 * kc + 2 * i + 1, kg)] = od;
+                }
             }
         }
     };
@@ -421,18 +437,35 @@ __global__ __launch_bounds__(256 * KS) void part_mfma_kernel(const PartArgs a) {
         // and 32 pm + 16 + 4 grp + {0..3}; each V fragment feeds QW MFMAs
         // (kept opaque so that the 2 NCB NPM addresses are formed in the loop, one ALU op
         // each, not held in registers across it)
-        int vx = vt_x_l;
-        asm volatile("" : "+v"(vx));
+        if constexpr (D == 128) {
+            // unit vt_pair(16 cb + col, 4 pm + grp) = 8 (16 cb + col) + ((grp ^ (col >> 1)) ^ (4 pm ^ cb)):
+            // a lane part XORed with an instruction constant, plus an instruction row
+            int px = grp ^ (col >> 1);
+            asm volatile("" : "+v"(px));
+            const u32x4 *vt4 = reinterpret_cast<const u32x4 *>(vt_lds) + 8 * col;
 #pragma unroll
-        for (int cb = 0; cb < NCB; ++cb) {
+            for (int cb = 0; cb < NCB; ++cb) {
 #pragma unroll
-            for (int pm = 0; pm < NPM; ++pm) {
-                const int rowc = CPS * cb * 32;
-                const uint2 lo = vt_lds[((vx ^ ((8 * pm) ^ vt_swz(CPS * cb))) + vt_row_l) + rowc];
-                const uint2 hi = vt_lds[((vx ^ ((8 * pm + 4) ^ vt_swz(CPS * cb))) + vt_row_l) + rowc];
-                const bf16x8_t vv = __builtin_bit_cast(bf16x8_t, u32x4{lo.x, lo.y, hi.x, hi.y});
+                for (int pm = 0; pm < NPM; ++pm) {
+                    const bf16x8_t vv = __builtin_bit_cast(bf16x8_t, vt4[128 * cb + (px ^ ((4 * pm) ^ cb))]);
 #pragma unroll
-                for (int b = 0; b < QW; ++b) o[b][cb] = mfma16(vv, pf[b][pm], o[b][cb]);
+                    for (int b = 0; b < QW; ++b) o[b][cb] = mfma16(vv, pf[b][pm], o[b][cb]);
+                }
+            }
+        } else {
+            int vx = vt_x_l;
+            asm volatile("" : "+v"(vx));
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb) {
+#pragma unroll
+                for (int pm = 0; pm < NPM; ++pm) {
+                    const int rowc = CPS * cb * 32;
+                    const uint2 lo = vt_lds[((vx ^ ((8 * pm) ^ vt_swz(CPS * cb))) + vt_row_l) + rowc];
+                    const uint2 hi = vt_lds[((vx ^ ((8 * pm + 4) ^ vt_swz(CPS * cb))) + vt_row_l) + rowc];
+                    const bf16x8_t vv = __builtin_bit_cast(bf16x8_t, u32x4{lo.x, lo.y, hi.x, hi.y});
+#pragma unroll
+                    for (int b = 0; b < QW; ++b) o[b][cb] = mfma16(vv, pf[b][pm], o[b][cb]);
+                }
             }
         }
     };
