@@ -307,6 +307,12 @@ __global__ __launch_bounds__(256 * KS) void part_mfma_kernel(const PartArgs a) {
     constexpr int RPS = Geo::RPS, CPS = 16 / RPS;
     const int vt_row_l = (col / RPS) * 32;
     const int vt_x_l = ((col % RPS) * Geo::UPR + grp) ^ vt_swz(col / RPS);
+    // D = 128: byte offset of this lane's pair unit (channel 16 cb + col, pair 4 pm + grp) within
+    // a 16-channel block, for each of the 8 values of the instruction constant (4 pm) ^ cb
+    int pv_off[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) pv_off[c] = 16 * (8 * col + ((grp ^ (col >> 1)) ^ c));
+    const bf16x8_t ones8 = __builtin_bit_cast(bf16x8_t, u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
 
     // NPF steps in flight (2 at d 128; 1 at d 512, where a tile is 8 registers x 4 per
     // thread and operand): step it + NPF is loaded into the registers that step it was staged
@@ -419,19 +425,21 @@ __global__ __launch_bounds__(256 * KS) void part_mfma_kernel(const PartArgs a) {
                 }
             }
             const float mc = (m_run[b] == -INFINITY) ? 0.f : m_run[b] * c2;
-            float psum = 0.f;
 #pragma unroll
             for (int pm = 0; pm < NPM; ++pm) {
 #pragma unroll
                 for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const float p = fast_exp2(__builtin_fmaf(sacc[b][2 * pm + hh][r], c2, -mc));
-                        psum += p;
-                        pf[b][pm][4 * hh + r] = (__bf16)p;
-                    }
+                    for (int r = 0; r < 4; ++r)
+                        pf[b][pm][4 * hh + r] = (__bf16)fast_exp2(__builtin_fmaf(sacc[b][2 * pm + hh][r], c2, -mc));
             }
-            l_run[b] += psum;
+            // the tile's weight sum of each column, from the same bf16 weights that PV uses:
+            // a ones matrix times P^T puts the column's sum over all the tile's keys in every
+            // lane of the column, so no lane adds or reduces them
+            f32x4_t ls = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int pm = 0; pm < NPM; ++pm) ls = mfma16(ones8, pf[b][pm], ls);
+            l_run[b] += ls[0];
         }
         // O^T += V^T P^T: A = V^T rows (channels 16 cb + col), keys 32 pm + 4 grp + {0..3}
         // and 32 pm + 16 + 4 grp + {0..3}; each V fragment feeds QW MFMAs
@@ -439,15 +447,14 @@ __global__ __launch_bounds__(256 * KS) void part_mfma_kernel(const PartArgs a) {
         // each, not held in registers across it)
         if constexpr (D == 128) {
             // unit vt_pair(16 cb + col, 4 pm + grp) = 8 (16 cb + col) + ((grp ^ (col >> 1)) ^ (4 pm ^ cb)):
-            // a lane part XORed with an instruction constant, plus an instruction row
-            int px = grp ^ (col >> 1);
-            asm volatile("" : "+v"(px));
-            const u32x4 *vt4 = reinterpret_cast<const u32x4 *>(vt_lds) + 8 * col;
+            // the lane's offset for the constant (4 pm) ^ cb, plus 2048 bytes per channel block
+            const char *vtb = reinterpret_cast<const char *>(vt_lds);
 #pragma unroll
             for (int cb = 0; cb < NCB; ++cb) {
 #pragma unroll
                 for (int pm = 0; pm < NPM; ++pm) {
-                    const bf16x8_t vv = __builtin_bit_cast(bf16x8_t, vt4[128 * cb + (px ^ ((4 * pm) ^ cb))]);
+                    const bf16x8_t vv = __builtin_bit_cast(
+                        bf16x8_t, *reinterpret_cast<const u32x4 *>(vtb + pv_off[(4 * pm) ^ cb] + 2048 * cb));
 #pragma unroll
                     for (int b = 0; b < QW; ++b) o[b][cb] = mfma16(vv, pf[b][pm], o[b][cb]);
                 }
@@ -544,13 +551,11 @@ __global__ __launch_bounds__(256 * KS) void part_mfma_kernel(const PartArgs a) {
         m_run[0] = m;
     }
 
-    // combine the four key groups' partial sums of each column; write the normalised bf16
-    // output (a direct call: the one split is the whole result, with the merge's arithmetic)
-    // or the partials
+    // write the normalised bf16 output (a direct call: the one split is the whole result, with
+    // the merge's arithmetic) or the partials
 #pragma unroll
     for (int b = 0; b < QW; ++b) {
-        float l_tot = l_run[b] + __shfl_xor(l_run[b], 16);
-        l_tot = l_tot + __shfl_xor(l_tot, 32);
+        const float l_tot = l_run[b];      // already the column's sum in every lane of it
         if (a.direct) {
             if (col_ok[b]) {
                 const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
