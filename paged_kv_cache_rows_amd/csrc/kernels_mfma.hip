@@ -258,17 +258,15 @@ __global__ __launch_bounds__(256 * KS) void part_mfma_kernel(const PartArgs a) {
     uint16_t *const k_st0 = k_lds_all[0][ksub];
     uint2 *const vt_st0 = vt_lds_all[0][ksub];
     u32x4 kreg0[KPT], vreg0[KPT], kreg1[KPT], vreg1[KPT];
-    auto load_tile = [&](int tb, u32x4 (&kreg)[KPT], u32x4 (&vreg)[KPT]) {
+    // this thread's pieces of sub-tile tb of one operand (K or V pages)
+    auto load_one = [&](int tb, const uint16_t *pages, u32x4 (&r)[KPT]) {
         if (MODE == 0) {
             // the whole tile lies in one page
             const int idx = tb / P;
             const int pg = max(t_lds[idx - idx0], 0);
             const size_t base = (size_t)pg * page_elems + head_off + (size_t)(tb - idx * P + KPT * kq) * D + 8 * kc;
 #pragma unroll
-            for (int u = 0; u < KPT; ++u) {
-                kreg[u] = *reinterpret_cast<const u32x4 *>(a.k_pages + base + (size_t)u * D);
-                vreg[u] = *reinterpret_cast<const u32x4 *>(a.v_pages + base + (size_t)u * D);
-            }
+            for (int u = 0; u < KPT; ++u) r[u] = *reinterpret_cast<const u32x4 *>(pages + base + (size_t)u * D);
         } else {
 #pragma unroll
             for (int u = 0; u < KPT; ++u) {
@@ -284,10 +282,13 @@ __global__ __launch_bounds__(256 * KS) void part_mfma_kernel(const PartArgs a) {
                     pg = (idx < a.stride && (unsigned)tp < (unsigned)a.num_pages) ? tp : -1;
                 }
                 const size_t e = (size_t)max(pg, 0) * page_elems + head_off + (size_t)off * D + 8 * kc;
-                kreg[u] = *reinterpret_cast<const u32x4 *>(a.k_pages + e);
-                vreg[u] = *reinterpret_cast<const u32x4 *>(a.v_pages + e);
+                r[u] = *reinterpret_cast<const u32x4 *>(pages + e);
             }
         }
+    };
+    auto load_tile = [&](int tb, u32x4 (&kreg)[KPT], u32x4 (&vreg)[KPT]) {
+        load_one(tb, a.k_pages, kreg);
+        load_one(tb, a.v_pages, vreg);
     };
 
     f32x4_t o[QW][NCB];
@@ -300,6 +301,10 @@ __global__ __launch_bounds__(256 * KS) void part_mfma_kernel(const PartArgs a) {
         l_run[b] = 0.f;
     }
     const float c2 = a.scale_log2;
+    // a running max is raised only when a score passes it by more than this (8 in the log2
+    // domain): the weights then stay below 2^8, which bf16 and the fp32 sums hold exactly
+    // as well as weights below 1, and most tiles skip the cross-lane max and the rescale
+    const float slack = fminf(8.0f / c2, 3.0e38f);      // finite, so that -inf + slack stays -inf
 
     // V^T operand reads (channel 16 cb + col, unit 8 pm + 4 hh + grp): vt_swz is linear over
     // GF(2) and the row number 16 cb / RPS + col / RPS has disjoint bit fields, so the unit
@@ -322,15 +327,18 @@ __global__ __launch_bounds__(256 * KS) void part_mfma_kernel(const PartArgs a) {
     const int kt_last = kt_first + (nt - 1) * KT;
     const int nsteps = (nt + KS - 1) / KS;
     // stage step it's sub-tile of this thread from (kreg, vreg) into buffer buf
-    auto stage = [&](int it, const u32x4 (&kreg)[KPT], const u32x4 (&vreg)[KPT], int buf) {
-        const int ts = kt_first + (it * KS + ksub) * KT;          // sub-tile this thread stages
+    // stage K rows as loaded into buffer buf
+    auto stage_k = [&](const u32x4 (&kreg)[KPT], int buf) {
         uint16_t *const k_st = k_st0 + buf * KBUF;
-        uint2 *const vt_st = vt_st0 + buf * VBUF;
-        // stage: K rows as loaded; V transposed into 4-key units, keys outside [kbeg, kend)
-        // zeroed (they may be unused slots holding NaN)
 #pragma unroll
         for (int u = 0; u < KPT; ++u)
             *reinterpret_cast<u32x4 *>(k_st + (KPT * kq + u) * KRS + 8 * kc) = kreg[u];
+    };
+    // stage V of step it transposed into 4-key units of buffer buf, keys outside [kbeg, kend)
+    // zeroed (they may be unused slots holding NaN)
+    auto stage_v = [&](int it, const u32x4 (&vreg)[KPT], int buf) {
+        const int ts = kt_first + (it * KS + ksub) * KT;          // sub-tile this thread stages
+        uint2 *const vt_st = vt_st0 + buf * VBUF;
         const bool inside = ts >= kbeg && ts + KT <= kend;
 #pragma unroll
         for (int h = 0; h < KPT / 4; ++h) {
@@ -363,15 +371,18 @@ __global__ __launch_bounds__(256 * KS) void part_mfma_kernel(const PartArgs a) {
             }
         }
     };
+    auto stage = [&](int it, const u32x4 (&kreg)[KPT], const u32x4 (&vreg)[KPT], int buf) {
+        stage_k(kreg, buf);
+        stage_v(it, vreg, buf);
+    };
     auto ts_of = [&](int it) { return kt_first + (it * KS + ksub) * KT; };
     // compute step it's sub-tile of this wave from buffer buf
-    auto compute = [&](int it, int buf) {
+    // S^T of step it's sub-tile for this wave's query columns, from K buffer buf; each K
+    // fragment feeds QW MFMAs (a padded step past the split computes nothing)
+    auto qk = [&](int it, int buf, f32x4_t (&sacc)[QW][NB]) {
         const int tb = kt_first + (it * KS + ksub) * KT;          // sub-tile this wave computes
-        if (tb >= kend) return;          // a padded step past the split: nothing to add
+        if (tb >= kend) return;
         const uint16_t *const k_lds = k_st0 + buf * KBUF;
-        const uint2 *const vt_lds = vt_st0 + buf * VBUF;
-        // S^T for this wave's query columns; each K fragment feeds QW MFMAs
-        f32x4_t sacc[QW][NB];
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
 #pragma unroll
@@ -383,6 +394,13 @@ __global__ __launch_bounds__(256 * KS) void part_mfma_kernel(const PartArgs a) {
                 for (int b = 0; b < QW; ++b) sacc[b][nb] = mfma16(kf, qf[b][kb], sacc[b][nb]);
             }
         }
+    };
+    // mask, online softmax and O^T += V^T P^T of step it's sub-tile, from its scores and V
+    // buffer buf
+    auto smpv = [&](int it, int buf, f32x4_t (&sacc)[QW][NB]) {
+        const int tb = kt_first + (it * KS + ksub) * KT;
+        if (tb >= kend) return;
+        const uint2 *const vt_lds = vt_st0 + buf * VBUF;
         const bool full = tb >= kbeg && tb + KT <= kend && tb + KT - 1 <= hi_full && tb >= lo_full;
         bf16x8_t pf[QW][NPM];
 #pragma unroll
@@ -408,10 +426,10 @@ __global__ __launch_bounds__(256 * KS) void part_mfma_kernel(const PartArgs a) {
                         tmax = fmaxf(tmax, x);
                     }
             }
-            // the running max of a column moves only when one of its scores exceeds it (rare
-            // after the first tiles): only then is the tile max reduced over the column's four
-            // lane groups and the sums rescaled
-            if (__builtin_amdgcn_ballot_w64(tmax > m_run[b])) {
+            // the running max of a column moves only when one of its scores passes it by more
+            // than the slack (rare after the first tile): only then is the tile max reduced over
+            // the column's four lane groups and the sums rescaled
+            if (__builtin_amdgcn_ballot_w64(tmax > m_run[b] + slack)) {
                 tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
                 tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
                 const float m_new = fmaxf(m_run[b], tmax);
@@ -476,6 +494,11 @@ __global__ __launch_bounds__(256 * KS) void part_mfma_kernel(const PartArgs a) {
             }
         }
     };
+    auto compute = [&](int it, int buf) {
+        f32x4_t sacc[QW][NB];
+        qk(it, buf, sacc);
+        smpv(it, buf, sacc);
+    };
     // loads for step it + NPF go into the registers step it was staged from
     auto step = [&](int it, u32x4 (&kreg)[KPT], u32x4 (&vreg)[KPT]) {
         lds_fence();
@@ -486,23 +509,53 @@ __global__ __launch_bounds__(256 * KS) void part_mfma_kernel(const PartArgs a) {
     };
     load_tile(min(ts_of(0), kt_last), kreg0, vreg0);
     if constexpr (NBUF == 2) {
-        static_assert(NPF == 2, "two tile buffers go with two register sets");
-        // register set r holds steps of parity r; step it + 1 is staged into the other buffer
-        // while step it is computed, and the registers it came from take step it + 3.  The
-        // first loads keep their issue order, so every wait is for the older set only.
+        static_assert(NPF == 2, "two tile buffers go with two register sets per operand");
+        // Software pipeline over two K and two V buffers.  Step it computes the scores of step
+        // it + 1 (MFMA) before the softmax and PV of step it, whose scores came from the step
+        // before: the MFMAs and the softmax of one wave are independent and overlap.  K is
+        // staged two steps ahead and V one step ahead, each into the buffer its previous
+        // reader released before the last barrier; register set r of an operand holds the
+        // steps of parity r, and the loads are issued in one fixed order (K it + 4, then V
+        // it + 3), so every wait is for the oldest set only.
+        u32x4 (&k0)[KPT] = kreg0, (&k1)[KPT] = kreg1, (&v0)[KPT] = vreg0, (&v1)[KPT] = vreg1;
+        load_one(min(ts_of(0), kt_last), a.k_pages, k0);
         asm volatile("" ::: "memory");
-        load_tile(min(ts_of(1), kt_last), kreg1, vreg1);
-        stage(0, kreg0, vreg0, 0);
-        load_tile(min(ts_of(2), kt_last), kreg0, vreg0);
+        load_one(min(ts_of(1), kt_last), a.k_pages, k1);
+        asm volatile("" ::: "memory");
+        load_one(min(ts_of(0), kt_last), a.v_pages, v0);
+        asm volatile("" ::: "memory");
+        stage_k(k0, 0);
+        load_one(min(ts_of(2), kt_last), a.k_pages, k0);
+        asm volatile("" ::: "memory");
+        stage_k(k1, 1);
+        load_one(min(ts_of(1), kt_last), a.v_pages, v1);
+        asm volatile("" ::: "memory");
+        load_one(min(ts_of(3), kt_last), a.k_pages, k1);
+        asm volatile("" ::: "memory");
+        stage_v(0, v0, 0);
+        load_one(min(ts_of(2), kt_last), a.v_pages, v0);
+        asm volatile("" ::: "memory");
         lds_fence();
+        f32x4_t s0[QW][NB], s1[QW][NB];
+        qk(0, 0, s0);
         for (int it = 0; it < nsteps; it += 2) {
-            stage(it + 1, kreg1, vreg1, 1);
-            load_tile(min(ts_of(it + 3), kt_last), kreg1, vreg1);
-            compute(it, 0);
+            qk(it + 1, 1, s1);
+            smpv(it, 0, s0);
+            stage_k(k0, 0);                                   // K(it + 2)
+            load_one(min(ts_of(it + 4), kt_last), a.k_pages, k0);
+            asm volatile("" ::: "memory");
+            stage_v(it + 1, v1, 1);                           // V(it + 1)
+            load_one(min(ts_of(it + 3), kt_last), a.v_pages, v1);
+            asm volatile("" ::: "memory");
             lds_fence();
-            stage(it + 2, kreg0, vreg0, 0);
-            load_tile(min(ts_of(it + 4), kt_last), kreg0, vreg0);
-            compute(it + 1, 1);
+            qk(it + 2, 0, s0);
+            smpv(it + 1, 1, s1);
+            stage_k(k1, 1);                                   // K(it + 3)
+            load_one(min(ts_of(it + 5), kt_last), a.k_pages, k1);
+            asm volatile("" ::: "memory");
+            stage_v(it + 2, v0, 0);                           // V(it + 2)
+            load_one(min(ts_of(it + 4), kt_last), a.v_pages, v0);
+            asm volatile("" ::: "memory");
             lds_fence();
         }
     } else if (NPF == 2) {
