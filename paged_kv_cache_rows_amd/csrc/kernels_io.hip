@@ -134,32 +134,66 @@ __global__ __launch_bounds__(64) void merge_kernel(const MergeArgs a) {
         }
         const float2 *ml = reinterpret_cast<const float2 *>(a.ws_ml) + (size_t)vec * a.n_splits;
         const float *acc = a.ws_acc + (size_t)vec * a.n_splits * D + cw * CW + cb * 8;
-        for (int i = i_begin + lane; i < n; i += 64) M = fmaxf(M, ml[i].x);
-        M = wave_max(M);
-        if (M != -INFINITY) {
-            for (int i0 = i_begin; i0 < n; i0 += 4 * SG) {
-                float4 x[4][2];
-                float w[4];
+        if (n - i_begin <= 4 * SG) {
+            // one pass (every decode and verify plan here): the partials and their (m, l) are
+            // loaded together, before the max is known, so the row costs one round trip to
+            // memory after the length, not two
+            float4 x[4][2];
+            float2 m_l[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int i = i_begin + u * SG + sg;
+                // a padded slot rereads the row's first split, which is always written (a zero
+                // weight must never meet an unwritten, possibly NaN, split)
+                const int ic = i < n ? i : i_begin;
+                m_l[u] = ml[ic];
+                const float4 *src = reinterpret_cast<const float4 *>(acc + (size_t)ic * D);
+                x[u][0] = src[0];
+                x[u][1] = src[1];
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) M = fmaxf(M, m_l[u].x);
+            M = wave_max(M);
+            if (M != -INFINITY) {
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
-                    const int i = i0 + u * SG + sg;
-                    const bool in = i < n;
-                    // a padded slot rereads the row's first split, which is always written
-                    // (a zero weight must never meet an unwritten, possibly NaN, split)
-                    const int ic = in ? i : i_begin;
-                    const float2 m_l = ml[ic];
-                    const float4 *src = reinterpret_cast<const float4 *>(acc + (size_t)ic * D);
-                    x[u][0] = src[0];
-                    x[u][1] = src[1];
-                    w[u] = (in && m_l.x != -INFINITY) ? fast_exp2(m_l.x - M) : 0.f;
-                    if (cb == 0) den += w[u] * m_l.y;
+                    const bool in = i_begin + u * SG + sg < n;
+                    const float w = (in && m_l[u].x != -INFINITY) ? fast_exp2(m_l[u].x - M) : 0.f;
+                    if (cb == 0) den += w * m_l[u].y;
+                    num[0] += w * x[u][0].x; num[1] += w * x[u][0].y;
+                    num[2] += w * x[u][0].z; num[3] += w * x[u][0].w;
+                    num[4] += w * x[u][1].x; num[5] += w * x[u][1].y;
+                    num[6] += w * x[u][1].z; num[7] += w * x[u][1].w;
                 }
-#pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    num[0] += w[u] * x[u][0].x; num[1] += w[u] * x[u][0].y;
-                    num[2] += w[u] * x[u][0].z; num[3] += w[u] * x[u][0].w;
-                    num[4] += w[u] * x[u][1].x; num[5] += w[u] * x[u][1].y;
-                    num[6] += w[u] * x[u][1].z; num[7] += w[u] * x[u][1].w;
+            }
+        } else {
+            for (int i = i_begin + lane; i < n; i += 64) M = fmaxf(M, ml[i].x);
+            M = wave_max(M);
+            if (M != -INFINITY) {
+                for (int i0 = i_begin; i0 < n; i0 += 4 * SG) {
+                    float4 x[4][2];
+                    float w[4];
+    #pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        const int i = i0 + u * SG + sg;
+                        const bool in = i < n;
+                        // a padded slot rereads the row's first split, which is always written
+                        // (a zero weight must never meet an unwritten, possibly NaN, split)
+                        const int ic = in ? i : i_begin;
+                        const float2 m_l = ml[ic];
+                        const float4 *src = reinterpret_cast<const float4 *>(acc + (size_t)ic * D);
+                        x[u][0] = src[0];
+                        x[u][1] = src[1];
+                        w[u] = (in && m_l.x != -INFINITY) ? fast_exp2(m_l.x - M) : 0.f;
+                        if (cb == 0) den += w[u] * m_l.y;
+                    }
+    #pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        num[0] += w[u] * x[u][0].x; num[1] += w[u] * x[u][0].y;
+                        num[2] += w[u] * x[u][0].z; num[3] += w[u] * x[u][0].w;
+                        num[4] += w[u] * x[u][1].x; num[5] += w[u] * x[u][1].y;
+                        num[6] += w[u] * x[u][1].z; num[7] += w[u] * x[u][1].w;
+                    }
                 }
             }
         }
