@@ -97,10 +97,19 @@ class DecodeSetup:
         self.binding = binding
         self.kv_bytes = sum(self.c.lengths) * w.kv_bytes_per_token
 
+    fused = True
+
     def step(self):
+        """One layer of the decode: the new row of each stream written into its page slot and
+        attended, in one paged_attn_decode_put call (fused) or as kv_rows_put followed by
+        paged_attn_decode (the same work and the same bytes)."""
         b, c = self.binding, self.c
-        b.rows_put(c.pool, c.table, c.seq_len, self.k_new, self.v_new, c.max_seq_len)
-        b.decode(c.pool, self.q, c.table, c.seq_len, c.max_seq_len, out=self.out, workspace=self.ws)
+        if self.fused:
+            b.decode_put(c.pool, self.q, c.table, c.seq_len, c.max_seq_len, self.k_new, self.v_new,
+                         out=self.out, workspace=self.ws)
+        else:
+            b.rows_put(c.pool, c.table, c.seq_len, self.k_new, self.v_new, c.max_seq_len)
+            b.decode(c.pool, self.q, c.table, c.seq_len, c.max_seq_len, out=self.out, workspace=self.ws)
 
     def attention_only(self):
         c = self.c
@@ -396,6 +405,14 @@ def main():
     value = setup.kv_bytes / (ms_step * 1e-3) / 1e9
     achieved = setup.kv_bytes / (part_ms * 1e-3) / 1e9
     traffic = measured_traffic()
+    # the same step as two calls (kv_rows_put, then paged_attn_decode), in interleaved rounds
+    # with the fused call
+    fused_ms, unfused_ms = [], []
+    for _ in range(3):
+        for fused, acc in ((True, fused_ms), (False, unfused_ms)):
+            setup.fused = fused
+            acc.append(timed_steps(setup, 30, 3, torch, binding)[0])
+    setup.fused = True
     log(f"[bench] {ms_step * 1e3:.1f} us/step, part kernel {part_ms * 1e3:.1f} us, {achieved:.0f} GB/s")
 
     result = {
@@ -414,7 +431,7 @@ def main():
         "config": {
             "workload": f"{w.name}: 12 streams, contexts U[32768, 40960] (seed 2002), 8 KV / 64 query "
                         f"heads, head_dim 128, bf16 K/V, pages of 512 shuffled over a pool with 10% NaN "
-                        f"spares; step = kv_rows_put (1 row/stream) + paged_attn_decode"
+                        f"spares; step = paged_attn_decode_put (the new row of each stream written into its page and attended, one call)"
             if args.fixed_length is None else
             f"{w.name}: 12 streams x {args.fixed_length}, otherwise as the batched decode",
             "streams": w.streams, "kv_heads": w.kv_heads, "q_heads": w.q_heads, "head_dim": w.head_dim,
@@ -422,6 +439,10 @@ def main():
             "kv_bytes_per_step": setup.kv_bytes,
         },
         "us_per_layer": round(ms_step * 1e3, 2),
+        "two_call_step": {"us_per_layer": round(sorted(unfused_ms)[1] * 1e3, 2),
+                          "fused_us_per_layer": round(sorted(fused_ms)[1] * 1e3, 2),
+                          "note": "kv_rows_put + paged_attn_decode against paged_attn_decode_put, medians of "
+                                  "3 interleaved rounds of 30 steps"},
         "roofline": {
             "bound": "hbm", "kernel": "part_valu_kernel<128,8,8>",
             "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",

@@ -184,6 +184,15 @@ kv_status paged_attn_workspace_size(const kv_pool *pool, const kv_layout *lay,
 kv_status paged_attn_decode(const kv_pool *pool, const kv_layout *lay, const kv_attn_args *a,
                             void *hip_stream);
 
+/* kv_rows_put of one new row per stream followed by paged_attn_decode, in one launch
+ * (TensorFold PR #1620, opening description, Writes and Reads bullets: a layer's new K/V row
+ * is copied into the pages, then attention reads through the table).  k_new, v_new: device
+ * bf16 [S][1][Hkv][D], written at position seq_len[s] - 1 exactly as kv_rows_put writes it;
+ * the output and every byte of the pool afterwards equal those of the two calls.  Errors as
+ * for decode, with KV_E_ARG for a null k_new or v_new. */
+kv_status paged_attn_decode_put(const kv_pool *pool, const kv_layout *lay, const kv_attn_args *a,
+                                const void *k_new, const void *v_new, void *hip_stream);
+
 /* The same for a speculative verify window of 1 <= R <= 8 causal rows per stream (TensorFold
  * PR #2730, What this changes: the pending token plus up to seven drafts, and the window
  * kernels accept any row count).  Row r sits at position L-R+r and sees keys up to and including itself.

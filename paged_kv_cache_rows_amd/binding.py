@@ -27,7 +27,8 @@ STATUS_NAMES = {0: "KV_OK", -1: "KV_E_ARG", -2: "KV_E_SHAPE", -3: "KV_E_NO_PAGES
 # The entry points include/kvpaged.h declares (checked against the built library's exports).
 EXPORTS = ("kv_pool_create", "kv_pool_destroy", "kv_page_lease", "kv_page_release", "kv_pool_set_lease_policy",
            "kv_pool_free_count", "kv_stream_pages", "kv_rows_put", "kv_pages_copy", "paged_attn_workspace_size",
-           "paged_attn_decode", "paged_attn_verify", "paged_attn_verify_tree", "paged_attn_prefill",
+           "paged_attn_decode", "paged_attn_decode_put", "paged_attn_verify", "paged_attn_verify_tree",
+           "paged_attn_prefill",
            "kv_set_part_events",
            "kv_last_error", "kv_abi_version")
 
@@ -79,6 +80,7 @@ def load(path: str = LIB_PATH):
         "kv_pages_copy": [c_void_p, c_void_p, c_void_p, c_int32, c_void_p],
         "paged_attn_workspace_size": [c_void_p, POINTER(Layout), POINTER(AttnArgs), POINTER(c_size_t)],
         "paged_attn_decode": [c_void_p, POINTER(Layout), POINTER(AttnArgs), c_void_p],
+        "paged_attn_decode_put": [c_void_p, POINTER(Layout), POINTER(AttnArgs), c_void_p, c_void_p, c_void_p],
         "paged_attn_verify": [c_void_p, POINTER(Layout), POINTER(AttnArgs), c_void_p],
         "paged_attn_verify_tree": [c_void_p, POINTER(Layout), POINTER(AttnArgs), c_void_p, c_void_p],
         "paged_attn_prefill": [c_void_p, POINTER(Layout), POINTER(AttnArgs), c_void_p],
@@ -257,6 +259,16 @@ def _attend(entry: str, pool: Pool, q: torch.Tensor, table: torch.Tensor, seq_le
 def decode(pool, q, table, seq_len, max_seq_len, **kw):
     """paged_attn_decode: one row per stream (q [S][1][Hq][D])."""
     return _attend("paged_attn_decode", pool, q, table, seq_len, max_seq_len, **kw)
+
+
+def decode_put(pool, q, table, seq_len, max_seq_len, k_new: torch.Tensor, v_new: torch.Tensor, **kw):
+    """paged_attn_decode_put: write k_new/v_new [S][1][Hkv][D] at position seq_len - 1 and
+    decode, in one launch (the same result as rows_put followed by decode)."""
+    shape = (int(q.shape[0]), 1, pool.kv_heads, pool.head_dim)
+    _need(k_new, torch.bfloat16, "k_new", shape)
+    _need(v_new, torch.bfloat16, "v_new", shape)
+    return _attend("paged_attn_decode_put", pool, q, table, seq_len, max_seq_len,
+                   extra=(_ptr(k_new), _ptr(v_new)), **kw)
 
 
 def verify(pool, q, table, seq_len, max_seq_len, **kw):

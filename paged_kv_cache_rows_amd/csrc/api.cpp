@@ -176,7 +176,8 @@ size_t workspace_bytes(const Plan &p) {
 }
 
 kv_status run_attention(const kv_pool *pool, const kv_layout *lay, const kv_attn_args *a, void *hip_stream,
-                        const char *who, const uint32_t *tree = nullptr) {
+                        const char *who, const uint32_t *tree = nullptr, const void *k_new = nullptr,
+                        const void *v_new = nullptr) {
     Plan p;
     kv_status st = make_plan(pool, lay, a, &p, who);
     if (st != KV_OK) return st;
@@ -210,6 +211,9 @@ kv_status run_attention(const kv_pool *pool, const kv_layout *lay, const kv_attn
     pa.chunk = p.chunk;
     pa.out = static_cast<uint16_t *>(a->out);
     pa.tree = tree;
+    pa.k_new = static_cast<const uint16_t *>(k_new);
+    pa.v_new = static_cast<const uint16_t *>(v_new);
+    if (k_new && p.mfma) return fail(KV_E_SHAPE, "%s: the fused row write has no MFMA kernel", who);
     pa.direct = (p.mfma && p.mp.direct) ? 1 : 0;
     const float scale = a->scale > 0.f ? a->scale : 1.0f / std::sqrt((float)p.D);
     pa.scale_log2 = scale * 1.4426950408889634f;
@@ -488,6 +492,13 @@ kv_status paged_attn_workspace_size(const kv_pool *pool, const kv_layout *lay, c
 kv_status paged_attn_decode(const kv_pool *pool, const kv_layout *lay, const kv_attn_args *a, void *hip_stream) {
     if (lay && lay->rows != 1) return fail(KV_E_ARG, "paged_attn_decode: rows %d != 1", lay->rows);
     return run_attention(pool, lay, a, hip_stream, "paged_attn_decode");
+}
+
+kv_status paged_attn_decode_put(const kv_pool *pool, const kv_layout *lay, const kv_attn_args *a,
+                                const void *k_new, const void *v_new, void *hip_stream) {
+    if (lay && lay->rows != 1) return fail(KV_E_ARG, "paged_attn_decode_put: rows %d != 1", lay->rows);
+    if (!k_new || !v_new) return fail(KV_E_ARG, "paged_attn_decode_put: k_new or v_new is null");
+    return run_attention(pool, lay, a, hip_stream, "paged_attn_decode_put", nullptr, k_new, v_new);
 }
 
 kv_status paged_attn_verify(const kv_pool *pool, const kv_layout *lay, const kv_attn_args *a, void *hip_stream) {

@@ -40,6 +40,9 @@ struct PartArgs {
     uint16_t *out;     // MFMA with n_splits == 1: bf16 output [S][R][Hq][D] written directly
     int direct;        //   (1), with no partials and no merge; 0: partials into the workspace
     float scale_log2;  // scale * log2(e)
+    // decode with the row write fused: k_new/v_new [S][1][Hkv][D] (NULL: no row to write)
+    const uint16_t *k_new;
+    const uint16_t *v_new;
 };
 
 // Arguments of the page copy (kept states): page dst[i] gets page src[i], K and V.

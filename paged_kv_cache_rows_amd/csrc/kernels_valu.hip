@@ -218,6 +218,28 @@ __global__ __launch_bounds__(64 * valu_waves<NQ>()) __attribute__((amdgpu_waves_
     lds_fence();
     const Loader ld{a.k_pages, a.v_pages, trow, t_lds, page_elems, head_off, P, idx0, lrow, wave,
                     a.ring_pages, a.stride, a.num_pages};
+    // decode with the row write fused (R = 1): the workgroup whose piece ends at the stream's
+    // length writes the new K/V row of its KV head into the page slot of position L - 1, as
+    // kv_rows_put does, before any of its loads; the barrier's workgroup-scope release and
+    // acquire order that write before the loads of its last batch, which read the slot
+    const bool put = a.k_new != nullptr && kend == L;
+    if (put) {
+        if (wave == 0 && lrow == 0) {
+            const size_t src = ((size_t)s * a.Hkv + kvh) * D + (size_t)lch * 8;
+            int idx = (L - 1) / P;
+            const int off = (L - 1) - idx * P;
+            if (a.ring_pages) idx %= a.ring_pages;
+            const int pg = idx < a.stride ? trow[idx] : -1;
+            if ((unsigned)pg < (unsigned)a.num_pages) {
+                const size_t dst = (size_t)pg * page_elems + head_off + (size_t)off * D;   // head_off has the lane's 8 channels
+                *reinterpret_cast<u32x4 *>(const_cast<uint16_t *>(a.k_pages) + dst) =
+                    *reinterpret_cast<const u32x4 *>(a.k_new + src);
+                *reinterpret_cast<u32x4 *>(const_cast<uint16_t *>(a.v_pages) + dst) =
+                    *reinterpret_cast<const u32x4 *>(a.v_new + src);
+            }
+        }
+        __syncthreads();
+    }
     u32x4 kr[NS], vr[NS];
 
     float m_run[VW], l_run[VW], acc[VW][8];

@@ -266,3 +266,16 @@ def test_library_follows_the_hand_worked_contiguous_sequence(lib):
         assert list(buf[:n.value]) == want
     assert lib.kv_pool_set_lease_policy(h, 7) == binding.KV_E_ARG
     lib.kv_pool_destroy(h)
+
+
+@host_only
+def test_decode_put_refuses_before_launch(lib):
+    d = binding.PoolDesc(8, 64, 4, 128, 2, 0x10000, 0x20000, None)
+    h = ctypes.c_void_p()
+    assert lib.kv_pool_create(ctypes.byref(d), ctypes.byref(h)) == 0
+    f = lib.paged_attn_decode_put
+    assert f(h, ctypes.byref(_layout(R=2)), ctypes.byref(_args()), 0x90000, 0xA0000, None) == binding.KV_E_ARG
+    assert f(h, ctypes.byref(_layout()), ctypes.byref(_args()), None, 0xA0000, None) == binding.KV_E_ARG
+    assert f(h, ctypes.byref(_layout()), ctypes.byref(_args(Hq=12)), 0x90000, 0xA0000, None) == binding.KV_E_SHAPE
+    assert lib.kv_last_error()
+    lib.kv_pool_destroy(h)
