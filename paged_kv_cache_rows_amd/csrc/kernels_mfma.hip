@@ -84,7 +84,9 @@ MfmaPlan mfma_plan(int D, int G, int R, int S, int Hkv, int max_seq_len, int win
     // one 16-column block per wave: two (QW = 2) halve the LDS reads per MFMA but need
     // about 280 registers, one wave per SIMD, and measured slower on every workload here
     p.qw = 1;
-    p.ks = 1;
+    // at d 128 a workgroup is 8 waves over two key sub-tiles (half the tile chain of a 4-wave
+    // one, and half the partials for the merge to read); a d 512 tile fills the LDS of one
+    p.ks = D == 128 ? 2 : 1;
     p.direct = false;
     p.tiles = (nq + 64 * p.qw - 1) / (64 * p.qw);
     const int kt = mfma_tile_keys(D);
@@ -99,20 +101,15 @@ MfmaPlan mfma_plan(int D, int G, int R, int S, int Hkv, int max_seq_len, int win
         p.direct = true;
         p.chunk = (span + kt - 1) / kt * kt;     // bounds the keys of one tile
         if (p.chunk < kt) p.chunk = kt;
-        p.ks = D == 128 ? 2 : 1;     // 8 waves over two key sub-tiles: half the tile chain
         return p;
     }
-    // aim at 2 (verify windows, bound by HBM) or 4 (prompt chunks, whose causal triangle
-    // leaves part of the grid idle) workgroups per CU over the whole call: long enough chunks
-    // to amortise the per-workgroup set-up, short enough to keep every CU busy
+    // aim at 8 (verify windows, bound by HBM) or 16 (prompt chunks, whose causal triangle
+    // leaves part of the grid idle) waves per CU over the whole call: long enough chunks to
+    // amortise the per-workgroup set-up, short enough to keep every CU busy.  The 8-wave
+    // workgroups of d 128 come half as many for the same waves (verify window: 35.6 -> 34.9 us
+    // for the part kernel against 4-wave ones, and a merge over 8 splits instead of 16)
     int64_t target = nq >= 256 ? 1024 : 512;
-    if (D == 128) {
-        // 8-wave workgroups over two key sub-tiles: half the workgroups for the same waves,
-        // so half the partials for the merge to read (verify window: 35.6 -> 34.9 us for the
-        // part kernel, and a merge over 8 splits instead of 16)
-        p.ks = 2;
-        target /= 2;
-    }
+    if (p.ks == 2) target /= 2;
     int64_t chunk = ((int64_t)span * groups + target - 1) / target;
     chunk = (chunk + kt - 1) / kt * kt;
     // at d 512 a chunk of 3 tiles (one round of about 190 workgroups on the 4-row verify at 9000
@@ -145,7 +142,7 @@ __global__ __launch_bounds__(256 * KS) void part_mfma_kernel(const PartArgs a) {
     constexpr int NPM = KT / 32;     // 32-key PV k-steps
 
     constexpr int NTH = 256 * KS;    // threads
-    static_assert(KS == 1 || (KS == 2 && D == 128), "key sub-tiles: 1, or 2 at D = 128");
+    static_assert((KS == 2) == (D == 128) && (KS == 1 || KS == 2), "key sub-tiles: 2 at D = 128, 1 at D = 512");
 
     // NBUF tile buffers: with two, a step stages the next step's tiles into one buffer while it
     // computes on the other (one barrier per step); one buffer stages and computes in turn
@@ -319,11 +316,8 @@ __global__ __launch_bounds__(256 * KS) void part_mfma_kernel(const PartArgs a) {
     for (int c = 0; c < 8; ++c) pv_off[c] = 16 * (8 * col + ((grp ^ (col >> 1)) ^ c));
     const bf16x8_t ones8 = __builtin_bit_cast(bf16x8_t, u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
 
-    // NPF steps in flight (2 at d 128; 1 at d 512, where a tile is 8 registers x 4 per
-    // thread and operand): step it + NPF is loaded into the registers that step it was staged
-    // from.  Step it covers sub-tiles KS it .. KS it + KS - 1; loads past the last sub-tile
-    // reread it (in bounds, never computed on), and sub-tiles past it are all masked out.
-    constexpr int NPF = D == 128 ? 2 : 1;
+    // Step it covers sub-tiles KS it .. KS it + KS - 1; loads past the last sub-tile reread it
+    // (in bounds, never computed on), and sub-tiles past it are all masked out.
     const int kt_last = kt_first + (nt - 1) * KT;
     const int nsteps = (nt + KS - 1) / KS;
     // stage step it's sub-tile of this thread from (kreg, vreg) into buffer buf
@@ -499,17 +493,16 @@ __global__ __launch_bounds__(256 * KS) void part_mfma_kernel(const PartArgs a) {
         qk(it, buf, sacc);
         smpv(it, buf, sacc);
     };
-    // loads for step it + NPF go into the registers step it was staged from
+    // d 512, one buffer and one step in flight (a tile is 8 registers x 4 per thread and
+    // operand): the loads for step it + 1 go into the registers step it was staged from
     auto step = [&](int it, u32x4 (&kreg)[KPT], u32x4 (&vreg)[KPT]) {
         lds_fence();
         stage(it, kreg, vreg, 0);
-        load_tile(min(ts_of(it + NPF), kt_last), kreg, vreg);
+        load_tile(min(ts_of(it + 1), kt_last), kreg, vreg);
         lds_fence();
         compute(it, 0);
     };
-    load_tile(min(ts_of(0), kt_last), kreg0, vreg0);
     if constexpr (NBUF == 2) {
-        static_assert(NPF == 2, "two tile buffers go with two register sets per operand");
         // Software pipeline over two K and two V buffers.  Step it computes the scores of step
         // it + 1 (MFMA) before the softmax and PV of step it, whose scores came from the step
         // before: the MFMAs and the softmax of one wave are independent and overlap.  K is
@@ -558,16 +551,8 @@ __global__ __launch_bounds__(256 * KS) void part_mfma_kernel(const PartArgs a) {
             asm volatile("" ::: "memory");
             lds_fence();
         }
-    } else if (NPF == 2) {
-        // keep the two first steps in issue order: the wait counts at the top of the loop
-        // assume buffer 0's loads are older than buffer 1's on every path into it
-        asm volatile("" ::: "memory");
-        load_tile(min(ts_of(1), kt_last), kreg1, vreg1);
-        for (int it = 0; it < nsteps; it += 2) {
-            step(it, kreg0, vreg0);
-            step(it + 1, kreg1, vreg1);
-        }
     } else {
+        load_tile(min(ts_of(0), kt_last), kreg0, vreg0);
         for (int it = 0; it < nsteps; ++it) step(it, kreg0, vreg0);
     }
 
@@ -657,9 +642,9 @@ hipError_t launch_part_mfma(int D, int G, const MfmaPlan &p, const PartArgs &arg
     if (items == 0) return hipSuccess;
     if (items > (int64_t)1 << 30) return hipErrorInvalidValue;
     a.per_xcd = (int)((items + 7) / 8);
-    if (p.qw != 1 || (p.ks == 2 && D != 128)) return hipErrorInvalidValue;
-    if (D == 128 && G == 4) return p.ks == 2 ? launch_dgq<128, 4, 1, 2>(a, st) : launch_dgq<128, 4, 1, 1>(a, st);
-    if (D == 128 && G == 8) return p.ks == 2 ? launch_dgq<128, 8, 1, 2>(a, st) : launch_dgq<128, 8, 1, 1>(a, st);
+    if (p.qw != 1 || p.ks != (D == 128 ? 2 : 1)) return hipErrorInvalidValue;
+    if (D == 128 && G == 4) return launch_dgq<128, 4, 1, 2>(a, st);
+    if (D == 128 && G == 8) return launch_dgq<128, 8, 1, 2>(a, st);
     if (D == 512 && G == 4) return launch_dgq<512, 4, 1, 1>(a, st);
     if (D == 512 && G == 8) return launch_dgq<512, 8, 1, 1>(a, st);
     return hipErrorInvalidValue;
