@@ -147,7 +147,7 @@ kv_status make_plan(const kv_pool *pool, const kv_layout *lay, const kv_attn_arg
     if (p->mfma) {
         if (!kvp::mfma_supported(p->D, p->G, p->R))
             return fail(KV_E_SHAPE, "%s: no MFMA kernel for head_dim %d, group %d, rows %d", who, p->D, p->G, p->R);
-        p->mp = kvp::mfma_plan(p->D, p->G, p->R, p->S, p->Hkv, lay->max_seq_len, a->window);
+        p->mp = kvp::mfma_plan(p->D, p->G, p->R, p->S, p->Hkv, pool->page_size, lay->max_seq_len, a->window);
         p->chunk = p->mp.chunk;
     } else {
         if (!kvp::valu_supported(p->D, p->G, nq))

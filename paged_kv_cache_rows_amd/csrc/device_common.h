@@ -79,7 +79,8 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // A 16-byte load of K/V page data with the nontemporal hint, for the decode kernel, which reads
 // every K/V byte of a call once: streaming it through the caches rather than keeping it there
 // raises the achieved HBM rate of the 12-stream decode from about 5.6 to 5.9-6.3 TB/s.  (The
-// MFMA kernel keeps plain loads: its query tiles reread each key tile from L2.)
+// MFMA kernel uses it at d 128 where a key tile has one reader; where several query tiles
+// reread a tile from L2, and at d 512, its loads stay plain.)
 __device__ __forceinline__ u32x4 stream_load(const uint16_t *p) {
     return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
 }

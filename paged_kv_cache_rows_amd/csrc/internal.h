@@ -97,7 +97,7 @@ struct MfmaPlan {
     bool direct;  // one split per query tile, covering exactly the keys its rows see; the bf16
                   // output is written by the part kernel (chunk then bounds that key span)
 };
-MfmaPlan mfma_plan(int D, int G, int R, int S, int Hkv, int max_seq_len, int window);
+MfmaPlan mfma_plan(int D, int G, int R, int S, int Hkv, int P, int max_seq_len, int window);
 
 hipError_t launch_rows_put(const RowsArgs &a, hipStream_t st);
 hipError_t launch_part_valu(int D, int G, int NQ, const PartArgs &a, int S, hipStream_t st);

@@ -24,6 +24,8 @@
 //    that every column sees in full skip the mask.
 //  * The workgroup writes an unnormalised partial (acc, m, l) per query vector, merged later
 //    in fixed chunk order.
+#include <algorithm>
+
 #include "internal.h"
 #include "device_common.h"
 
@@ -78,7 +80,7 @@ bool mfma_supported(int D, int G, int R) {
 // Query-column blocks per wave, query tiles and chunk length of one call.  Everything here is
 // a function of the call's shape (never of page ids or device lengths), so the chunk
 // boundaries, and with them the result, do not depend on where pages live.
-MfmaPlan mfma_plan(int D, int G, int R, int S, int Hkv, int max_seq_len, int window) {
+MfmaPlan mfma_plan(int D, int G, int R, int S, int Hkv, int P, int max_seq_len, int window) {
     MfmaPlan p;
     const int nq = R * G;
     // one 16-column block per wave: two (QW = 2) halve the LDS reads per MFMA but need
@@ -103,20 +105,52 @@ MfmaPlan mfma_plan(int D, int G, int R, int S, int Hkv, int max_seq_len, int win
         if (p.chunk < kt) p.chunk = kt;
         return p;
     }
-    // aim at 8 (verify windows, bound by HBM) or 16 (prompt chunks, whose causal triangle
-    // leaves part of the grid idle) waves per CU over the whole call: long enough chunks to
-    // amortise the per-workgroup set-up, short enough to keep every CU busy.  The 8-wave
-    // workgroups of d 128 come half as many for the same waves (verify window: 35.6 -> 34.9 us
-    // for the part kernel against 4-wave ones, and a merge over 8 splits instead of 16)
-    int64_t target = nq >= 256 ? 1024 : 512;
-    if (p.ks == 2) target /= 2;
+    // at d 512 a chunk of at least 3 tiles (one round of about 190 workgroups on the 4-row
+    // verify at 9000 keys: 29.3 -> 27.4 us; 2 tiles need a second round and take 38 us)
+    const int64_t lo = (D == 512 ? 3 : 4) * kt;
+    // the longest chunk whose page-table entries the kernel caches in LDS (longer ones read the
+    // table from memory per key piece); none if even the shortest does not fit
+    int64_t hi = ((int64_t)(MfmaGeom<128>::TC - 2) * P - kt) / kt * kt;
+    if (hi < lo) hi = (int64_t)1 << 40;
+    if (nq < 256) {
+        // Verify windows: every row sees about the same keys, so all workgroups of the call do
+        // the same work, and one of them fills a CU (137 KB of LDS at d 128; 4 waves of more
+        // than 256 registers at d 512): the call runs in rounds of 256 workgroups.  Take the
+        // chunk that minimises rounds x (time of one workgroup), a workgroup costing its K/V
+        // bytes at an even share of about 85 % of HBM plus about 5 us of start-up and drain
+        // (both measured on the 4-stream verify).  A round left nearly empty by the chunk
+        // count doubles the time: 4 streams x 36k keys in 9 chunks of 4096 (288 workgroups)
+        // took 161 us, in 8 of 4608 (256) 112 us.
+        const double us_per_key = 4.0 * D / (0.85 * 8000.0e3 / 256.0), t0 = 5.0;
+        double best = 0;
+        int64_t best_chunk = lo;
+        for (int64_t n = 1;; ++n) {
+            int64_t c = ((span + n - 1) / n + kt - 1) / kt * kt;
+            if (c < lo) c = lo;
+            if (c <= hi) {
+                int64_t ns = (max_seq_len + c - 1) / c;      // as the call's split count
+                if (window > 0) ns = std::min(ns, (span + c - 1) / c + 1);
+                const int64_t rounds = (groups * ns + 255) / 256;
+                const double t = (double)rounds * ((double)c * us_per_key + t0);
+                if (best == 0 || t < best) {
+                    best = t;
+                    best_chunk = c;
+                }
+            }
+            if (c == lo) break;
+        }
+        p.chunk = (int)best_chunk;
+        return p;
+    }
+    // Prompt-sized windows on few streams: aim at 16 waves per CU over the whole call (the
+    // causal triangle gives the query tiles unequal work, so several rounds keep the grid
+    // busy): long enough chunks to amortise the per-workgroup set-up, short enough to keep
+    // every CU busy.  The 8-wave workgroups of d 128 come half as many for the same waves.
+    const int64_t target = p.ks == 2 ? 512 : 1024;
     int64_t chunk = ((int64_t)span * groups + target - 1) / target;
     chunk = (chunk + kt - 1) / kt * kt;
-    // at d 512 a chunk of 3 tiles (one round of about 190 workgroups on the 4-row verify at 9000
-    // keys: 29.3 -> 27.4 us; 2 tiles need a second round and take 38 us)
-    const int lo = (D == 512 ? 3 : 4) * kt, hi = 64 * kt;
     if (chunk < lo) chunk = lo;
-    if (chunk > hi) chunk = hi;
+    if (chunk > std::min<int64_t>(hi, 64 * kt)) chunk = std::min<int64_t>(hi, 64 * kt);
     p.chunk = (int)chunk;
     return p;
 }
@@ -127,11 +161,15 @@ __device__ __forceinline__ f32x4_t mfma16(const bf16x8_t &a, const bf16x8_t &b, 
 
 // MODE 0: P % KT == 0 and the chunk's table entries cached in LDS (one lookup per tile);
 // MODE 1: entries cached, lookup per piece; MODE 2: lookup per piece in the global table.
+// NTL: K/V loads are nontemporal.  Used at d 128 where each key tile has one reader, so that
+// nothing is gained by keeping it in the caches (4 streams x 36k keys: 112 -> 96 us).  With
+// several query tiles per chunk the tiles reread it from L2, and at d 512 plain loads measured
+// faster (4-row verify at 9000 keys in pages of 37: 23.2 against 26.1 us), so those stay plain.
 // KS: key sub-tiles per iteration.  With KS = 2 the workgroup has 8 waves: waves 4 g .. 4 g + 3
 // compute sub-tile g of each 2 KT-key step with an online softmax of their own, and the two
 // states are combined through LDS at the end, which halves the tile chain of a workgroup
 // without splitting the keys over workgroups (no partials in memory).
-template <int D, int G, int QW, int MODE, int KS>
+template <int D, int G, int QW, int MODE, int KS, bool NTL>
 __global__ __launch_bounds__(256 * KS) void part_mfma_kernel(const PartArgs a) {
     using Geo = MfmaGeom<D>;
     constexpr int KT = Geo::KT, KRS = Geo::KRS, CB = Geo::CB, KPT = Geo::KPT, TC = Geo::TC;
@@ -255,6 +293,10 @@ __global__ __launch_bounds__(256 * KS) void part_mfma_kernel(const PartArgs a) {
     uint16_t *const k_st0 = k_lds_all[0][ksub];
     uint2 *const vt_st0 = vt_lds_all[0][ksub];
     u32x4 kreg0[KPT], vreg0[KPT], kreg1[KPT], vreg1[KPT];
+    auto ld16 = [](const uint16_t *p) {
+        if constexpr (NTL) return stream_load(p);
+        else return *reinterpret_cast<const u32x4 *>(p);
+    };
     // this thread's pieces of sub-tile tb of one operand (K or V pages)
     auto load_one = [&](int tb, const uint16_t *pages, u32x4 (&r)[KPT]) {
         if (MODE == 0) {
@@ -263,7 +305,7 @@ __global__ __launch_bounds__(256 * KS) void part_mfma_kernel(const PartArgs a) {
             const int pg = max(t_lds[idx - idx0], 0);
             const size_t base = (size_t)pg * page_elems + head_off + (size_t)(tb - idx * P + KPT * kq) * D + 8 * kc;
 #pragma unroll
-            for (int u = 0; u < KPT; ++u) r[u] = *reinterpret_cast<const u32x4 *>(pages + base + (size_t)u * D);
+            for (int u = 0; u < KPT; ++u) r[u] = ld16(pages + base + (size_t)u * D);
         } else {
 #pragma unroll
             for (int u = 0; u < KPT; ++u) {
@@ -279,7 +321,7 @@ __global__ __launch_bounds__(256 * KS) void part_mfma_kernel(const PartArgs a) {
                     pg = (idx < a.stride && (unsigned)tp < (unsigned)a.num_pages) ? tp : -1;
                 }
                 const size_t e = (size_t)max(pg, 0) * page_elems + head_off + (size_t)off * D + 8 * kc;
-                r[u] = *reinterpret_cast<const u32x4 *>(pages + e);
+                r[u] = ld16(pages + e);
             }
         }
     };
@@ -531,7 +573,14 @@ __global__ __launch_bounds__(256 * KS) void part_mfma_kernel(const PartArgs a) {
         lds_fence();
         f32x4_t s0[QW][NB], s1[QW][NB];
         qk(0, 0, s0);
-        for (int it = 0; it < nsteps; it += 2) {
+        // Steps it and it + 1 per iteration.  The last iterations (the second loop, the same
+        // body) neither load nor stage steps past the split, so that the split ends when its
+        // own data has arrived, not after loads that would only reread its last tile (4-stream
+        // verify at 9k keys: 32.4 -> 29.9 us).  The body is written out twice rather than
+        // guarded in one loop: conditional loads in the main loop would make every wait in it
+        // conservative, and a shared lambda put the step registers in scratch memory.
+        int it = 0;
+        for (; it + 6 <= nsteps; it += 2) {
             qk(it + 1, 1, s1);
             smpv(it, 0, s0);
             stage_k(k0, 0);                                   // K(it + 2)
@@ -548,6 +597,26 @@ __global__ __launch_bounds__(256 * KS) void part_mfma_kernel(const PartArgs a) {
             asm volatile("" ::: "memory");
             stage_v(it + 2, v0, 0);                           // V(it + 2)
             load_one(min(ts_of(it + 4), kt_last), a.v_pages, v0);
+            asm volatile("" ::: "memory");
+            lds_fence();
+        }
+        for (; it < nsteps; it += 2) {
+            qk(it + 1, 1, s1);
+            smpv(it, 0, s0);
+            if (it + 2 < nsteps) stage_k(k0, 0);
+            if (it + 4 < nsteps) load_one(min(ts_of(it + 4), kt_last), a.k_pages, k0);
+            asm volatile("" ::: "memory");
+            if (it + 1 < nsteps) stage_v(it + 1, v1, 1);
+            if (it + 3 < nsteps) load_one(min(ts_of(it + 3), kt_last), a.v_pages, v1);
+            asm volatile("" ::: "memory");
+            lds_fence();
+            qk(it + 2, 0, s0);
+            smpv(it + 1, 1, s1);
+            if (it + 3 < nsteps) stage_k(k1, 1);
+            if (it + 5 < nsteps) load_one(min(ts_of(it + 5), kt_last), a.k_pages, k1);
+            asm volatile("" ::: "memory");
+            if (it + 2 < nsteps) stage_v(it + 2, v0, 0);
+            if (it + 4 < nsteps) load_one(min(ts_of(it + 4), kt_last), a.v_pages, v0);
             asm volatile("" ::: "memory");
             lds_fence();
         }
@@ -619,18 +688,25 @@ __global__ __launch_bounds__(256 * KS) void part_mfma_kernel(const PartArgs a) {
     }
 }
 
-template <int D, int G, int QW, int KS>
+template <int D, int G, int QW, int KS, bool NTL>
 static hipError_t launch_dgq(const PartArgs &a, hipStream_t st) {
     using Geo = MfmaGeom<D>;
     const dim3 grid(8 * a.per_xcd);
     const bool cached = (a.chunk + Geo::KT) / a.P + 2 <= Geo::TC;
     if (cached && a.P % Geo::KT == 0)
-        hipLaunchKernelGGL((part_mfma_kernel<D, G, QW, 0, KS>), grid, dim3(256 * KS), 0, st, a);
+        hipLaunchKernelGGL((part_mfma_kernel<D, G, QW, 0, KS, NTL>), grid, dim3(256 * KS), 0, st, a);
     else if (cached)
-        hipLaunchKernelGGL((part_mfma_kernel<D, G, QW, 1, KS>), grid, dim3(256 * KS), 0, st, a);
+        hipLaunchKernelGGL((part_mfma_kernel<D, G, QW, 1, KS, NTL>), grid, dim3(256 * KS), 0, st, a);
     else
-        hipLaunchKernelGGL((part_mfma_kernel<D, G, QW, 2, KS>), grid, dim3(256 * KS), 0, st, a);
+        hipLaunchKernelGGL((part_mfma_kernel<D, G, QW, 2, KS, NTL>), grid, dim3(256 * KS), 0, st, a);
     return hipGetLastError();
+}
+
+template <int D, int G, int KS>
+static hipError_t launch_dg(const PartArgs &a, hipStream_t st) {
+    if constexpr (D == 128)
+        if (a.tiles == 1) return launch_dgq<D, G, 1, KS, true>(a, st);
+    return launch_dgq<D, G, 1, KS, false>(a, st);
 }
 
 hipError_t launch_part_mfma(int D, int G, const MfmaPlan &p, const PartArgs &args, int S, hipStream_t st) {
@@ -643,10 +719,10 @@ hipError_t launch_part_mfma(int D, int G, const MfmaPlan &p, const PartArgs &arg
     if (items > (int64_t)1 << 30) return hipErrorInvalidValue;
     a.per_xcd = (int)((items + 7) / 8);
     if (p.qw != 1 || p.ks != (D == 128 ? 2 : 1)) return hipErrorInvalidValue;
-    if (D == 128 && G == 4) return launch_dgq<128, 4, 1, 2>(a, st);
-    if (D == 128 && G == 8) return launch_dgq<128, 8, 1, 2>(a, st);
-    if (D == 512 && G == 4) return launch_dgq<512, 4, 1, 1>(a, st);
-    if (D == 512 && G == 8) return launch_dgq<512, 8, 1, 1>(a, st);
+    if (D == 128 && G == 4) return launch_dg<128, 4, 2>(a, st);
+    if (D == 128 && G == 8) return launch_dg<128, 8, 2>(a, st);
+    if (D == 512 && G == 4) return launch_dg<512, 4, 1>(a, st);
+    if (D == 512 && G == 8) return launch_dg<512, 8, 1>(a, st);
     return hipErrorInvalidValue;
 }
 

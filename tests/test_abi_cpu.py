@@ -213,6 +213,37 @@ def test_workspace_size_depends_on_shape_only(lib):
     lib.kv_pool_destroy(h)
 
 
+def _splits(lib, S, R, Hkv, G, D, P, max_len, window=0):
+    """Split count of an attention call, read from its workspace size."""
+    d = binding.PoolDesc(100000, P, Hkv, D, S, 0x10000, 0x20000, None)
+    h = ctypes.c_void_p()
+    assert lib.kv_pool_create(ctypes.byref(d), ctypes.byref(h)) == 0
+    lay = binding.Layout(S, R, 0x30000, (max_len + P - 1) // P, 0x40000, max_len, 0)
+    n = ctypes.c_size_t()
+    assert lib.paged_attn_workspace_size(h, ctypes.byref(lay), ctypes.byref(_args(Hq=Hkv * G, window=window)),
+                                         ctypes.byref(n)) == 0, lib.kv_last_error()
+    lib.kv_pool_destroy(h)
+    per_split = S * R * Hkv * G * (D + 2) * 4
+    assert n.value % per_split == 0
+    return n.value // per_split
+
+
+@pytest.mark.parametrize("S,R,Hkv,G,D,P,max_len,window,splits", [
+    (4, 8, 8, 8, 128, 512, 9200, 0, 8),      # the verify window: 4 x 8 x 8 = 256 workgroups, one round
+    (4, 8, 8, 8, 128, 512, 36800, 0, 8),     # 4096-key chunks would need 9 (288 workgroups, two rounds)
+    (4, 8, 8, 8, 128, 37, 36800, 0, 8),      # the same with pages of 37 (chunks still cached)
+    (12, 8, 8, 8, 128, 512, 40960, 0, 8),    # 96 groups: 768 workgroups, three whole rounds
+    (12, 2, 8, 8, 128, 512, 40960, 0, 8),    # 2 rows x GQA 8 = 16 query vectors: MFMA, as above
+    (1, 4, 2, 8, 512, 37, 9000, 0, 94),      # d 512: chunks of 3 tiles, 188 workgroups
+    (2, 8, 8, 8, 128, 512, 3000, 100, 2),    # window of 100: its keys fit one chunk, plus the edge
+])
+def test_verify_splits_fill_whole_rounds(lib, S, R, Hkv, G, D, P, max_len, window, splits):
+    # A verify window gives every workgroup about the same work and one workgroup fills a CU, so
+    # the call runs in rounds of 256 workgroups: the split count must not leave a round nearly
+    # empty.
+    assert _splits(lib, S, R, Hkv, G, D, P, max_len, window) == splits
+
+
 @host_only
 def test_rows_put_refuses_bad_layouts(lib):
     d = binding.PoolDesc(8, 64, 1, 128, 2, 0x10000, 0x20000, None)
