@@ -43,6 +43,19 @@ def test_verify_rows_parity(G, R, P):
     assert_close(attend("verify", c, q), oracle_for(c, q), f"verify G={G} R={R} P={P}")
 
 
+@pytest.mark.parametrize("L", [2000, 5000, 6100, 7000, 13000])
+@pytest.mark.parametrize("P", [64, 37])
+def test_verify_splits_of_many_step_counts(L, P):
+    # 4 streams x 8 KV heads: the plan cuts each stream into 8 chunks of about L / 8 keys, so a
+    # split runs 2, 5, 6, 7 or 13 two-tile steps: the pipeline's main loop, its tail without
+    # loads past the split, and the boundary between them; shorter streams end mid-chunk
+    w = _w(streams=4, kv_heads=8, group=8, rows=8, page_size=P, lengths=[L, L - 37, L // 2, 9])
+    say(f"verify splits L={L} P={P}")
+    c, _, _ = new_cache(w)
+    q = workloads.queries(w).cuda()
+    assert_close(attend("verify", c, q), oracle_for(c, q), f"verify L={L} P={P}")
+
+
 def test_verify_is_byte_equal_under_shuffles_and_repeat():
     w = _w(lengths=[2500, 1300, 800], streams=3, page_size=512)
     q = workloads.queries(w).cuda()
