@@ -455,8 +455,10 @@ __global__ __launch_bounds__(256 * KS) void part_mfma_kernel(const PartArgs a) {
                     for (int r = 0; r < 4; ++r) {
                         const int j = tb + 16 * nb + 4 * grp + r;
                         const int t = j - win0;             // window slot of the key, if >= 0
-                        const bool vis = col_ok[b] && j >= kbeg && j < kend && j <= p_col[b] && j >= lo_col[b] &&
-                                         (t < 0 || ((anc[b] >> (t & 31)) & 1u));
+                        // bitwise, not short-circuit, so that the test is straight-line selects
+                        // rather than a branch per score
+                        const bool vis = col_ok[b] & (j >= kbeg) & (j < kend) & (j <= p_col[b]) & (j >= lo_col[b]) &
+                                         ((t < 0) | (((anc[b] >> (t & 31)) & 1u) != 0));
                         const float x = vis ? sacc[b][nb][r] : -INFINITY;
                         sacc[b][nb][r] = x;
                         tmax = fmaxf(tmax, x);
