@@ -379,7 +379,6 @@ def main():
     import numpy as np
     import torch
 
-    import oracle
     from paged_kv_cache_rows_amd import binding, staging, workloads
 
     if not torch.cuda.is_available():
@@ -509,6 +508,7 @@ def main():
         calibration_copy(torch)
 
     if not args.no_cpu_baseline:
+        import oracle          # the CPU reference, used by this leg only
         log("[bench] cpu baseline (oracle)")
         result["cpu_baseline"] = cpu_baseline(setup, oracle, workloads)
     print(json.dumps(result), flush=True)
