@@ -86,8 +86,8 @@ typedef struct kv_layout {
 
 /* Attention arguments. */
 typedef struct kv_attn_args {
-    const void *q;           /* device bf16 [S][R][Hq][D] */
-    void *out;               /* device bf16 [S][R][Hq][D], written in full */
+    const void *q;           /* device bf16 [S][R][Hq][D], 16-byte aligned */
+    void *out;               /* device bf16 [S][R][Hq][D], 16-byte aligned, written in full */
     int32_t num_q_heads;     /* Hq, a multiple of Hkv; query head h reads KV head h / (Hq/Hkv) */
     float scale;             /* score scale; 0 means 1/sqrt(D) */
     int32_t window;          /* 0: full causal; W > 0: row at position p sees keys p-W+1 .. p */
@@ -146,10 +146,11 @@ kv_status kv_stream_pages(const kv_pool *pool, int32_t stream, int32_t *ids_out,
 
 /* Write each stream's R new K and V rows into their page slots (TensorFold PR #1620, opening
  * description, Writes bullet: the K/V rows a layer produces are copied into the pages).
- * k_new, v_new: device bf16 [S][R][Hkv][D].  Row r of stream s goes to position
- * seq_len[s] - R + r, i.e. page table[s][pos / P] (or ring slot (pos / P) % ring_pages) at
- * slot pos % P, for every KV head.  Rows at negative positions are skipped.  Every other byte
- * of the pool is left untouched.  Errors: KV_E_ARG (null pointers, bad sizes). */
+ * k_new, v_new: device bf16 [S][R][Hkv][D], 16-byte aligned.  Row r of stream s goes to
+ * position seq_len[s] - R + r, i.e. page table[s][pos / P] (or ring slot (pos / P) % ring_pages)
+ * at slot pos % P, for every KV head.  Rows at negative positions are skipped.  Every other
+ * byte of the pool is left untouched.  Errors: KV_E_ARG (null or misaligned pointers, bad
+ * sizes). */
 kv_status kv_rows_put(const kv_pool *pool, const kv_layout *lay, const void *k_new,
                       const void *v_new, void *hip_stream);
 
@@ -179,7 +180,7 @@ kv_status paged_attn_workspace_size(const kv_pool *pool, const kv_layout *lay,
  * 0..L-1, or the newest `window`), K and V read through the stream's page table.  Computed
  * with fp32 accumulation; the output is rounded to bf16 (nearest even).  Results depend only
  * on the logical cache, never on which physical pages hold it (bit for bit).
- * Errors: KV_E_ARG (R != 1, null pointers, Hq not a multiple of Hkv), KV_E_SHAPE (no kernel
+ * Errors: KV_E_ARG (R != 1, null or misaligned pointers, Hq not a multiple of Hkv), KV_E_SHAPE (no kernel
  * for this head_dim or group), KV_E_WORKSPACE (too small). */
 kv_status paged_attn_decode(const kv_pool *pool, const kv_layout *lay, const kv_attn_args *a,
                             void *hip_stream);
@@ -187,9 +188,9 @@ kv_status paged_attn_decode(const kv_pool *pool, const kv_layout *lay, const kv_
 /* kv_rows_put of one new row per stream followed by paged_attn_decode, in one launch
  * (TensorFold PR #1620, opening description, Writes and Reads bullets: a layer's new K/V row
  * is copied into the pages, then attention reads through the table).  k_new, v_new: device
- * bf16 [S][1][Hkv][D], written at position seq_len[s] - 1 exactly as kv_rows_put writes it;
- * the output and every byte of the pool afterwards equal those of the two calls.  Errors as
- * for decode, with KV_E_ARG for a null k_new or v_new. */
+ * bf16 [S][1][Hkv][D] (16-byte aligned), written at position seq_len[s] - 1 exactly as
+ * kv_rows_put writes it; the output and every byte of the pool afterwards equal those of the
+ * two calls.  Errors as for decode, with KV_E_ARG for a null or misaligned k_new or v_new. */
 kv_status paged_attn_decode_put(const kv_pool *pool, const kv_layout *lay, const kv_attn_args *a,
                                 const void *k_new, const void *v_new, void *hip_stream);
 

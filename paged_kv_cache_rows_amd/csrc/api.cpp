@@ -52,6 +52,9 @@ bool check_enabled() {
 
 int ceil_div(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
 
+// The kernels move rows of q, out and new K/V in 16-byte pieces.
+bool aligned16(const void *p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; }
+
 kv_status check_layout(const kv_pool *pool, const kv_layout *lay, const char *who) {
     if (!pool) return fail(KV_E_ARG, "%s: pool is null", who);
     if (!lay) return fail(KV_E_ARG, "%s: layout is null", who);
@@ -182,6 +185,9 @@ kv_status run_attention(const kv_pool *pool, const kv_layout *lay, const kv_attn
     kv_status st = make_plan(pool, lay, a, &p, who);
     if (st != KV_OK) return st;
     if (!a->q || !a->out) return fail(KV_E_ARG, "%s: q or out is null", who);
+    if (!aligned16(a->q) || !aligned16(a->out)) return fail(KV_E_ARG, "%s: q and out must be 16-byte aligned", who);
+    if ((k_new && !aligned16(k_new)) || (v_new && !aligned16(v_new)))
+        return fail(KV_E_ARG, "%s: k_new and v_new must be 16-byte aligned", who);
     const size_t need = workspace_bytes(p);
     if (!a->workspace || a->workspace_bytes < need)
         return fail(KV_E_WORKSPACE, "%s: workspace of %zu bytes, %zu needed", who, a->workspace_bytes, need);
@@ -453,6 +459,7 @@ kv_status kv_rows_put(const kv_pool *pool, const kv_layout *lay, const void *k_n
     kv_status st = check_layout(pool, lay, "kv_rows_put");
     if (st != KV_OK) return st;
     if (!k_new || !v_new) return fail(KV_E_ARG, "kv_rows_put: k_new or v_new is null");
+    if (!aligned16(k_new) || !aligned16(v_new)) return fail(KV_E_ARG, "kv_rows_put: k_new and v_new must be 16-byte aligned");
     hipStream_t hs = reinterpret_cast<hipStream_t>(hip_stream);
     if (lay->ring_pages && (int64_t)lay->rows > (int64_t)lay->ring_pages * pool->page_size)
         return fail(KV_E_ARG, "kv_rows_put: %d rows overrun a ring of %d x %d positions", lay->rows,

@@ -160,8 +160,8 @@ def _layout(S=1, R=1, stride=8, max_len=300, ring=0):
     return binding.Layout(S, R, 0x30000, stride, 0x40000, max_len, ring)
 
 
-def _args(Hq=16, window=0, ws=0x50000, nbytes=1 << 30, scale=0.0):
-    return binding.AttnArgs(0x60000, 0x70000, Hq, scale, window, ws, nbytes)
+def _args(Hq=16, window=0, ws=0x50000, nbytes=1 << 30, scale=0.0, q=0x60000, out=0x70000):
+    return binding.AttnArgs(q, out, Hq, scale, window, ws, nbytes)
 
 
 @pytest.mark.parametrize("entry,lay,args,status", [
@@ -173,6 +173,8 @@ def _args(Hq=16, window=0, ws=0x50000, nbytes=1 << 30, scale=0.0):
     ("paged_attn_decode", _layout(), _args(Hq=12), binding.KV_E_SHAPE),        # group 3: no kernel
     ("paged_attn_decode", _layout(), _args(nbytes=16), binding.KV_E_WORKSPACE),
     ("paged_attn_decode", _layout(), _args(ws=0x50010), binding.KV_E_ARG),     # workspace misaligned
+    ("paged_attn_decode", _layout(), _args(q=0x60008), binding.KV_E_ARG),      # q not 16-byte aligned
+    ("paged_attn_verify", _layout(R=4), _args(out=0x70002), binding.KV_E_ARG),  # out not 16-byte aligned
     ("paged_attn_decode", _layout(), _args(window=-1), binding.KV_E_ARG),
     ("paged_attn_decode", _layout(), _args(scale=-1.0), binding.KV_E_ARG),
     ("paged_attn_decode", _layout(ring=2), _args(), binding.KV_E_ARG),         # ring without a window
@@ -251,6 +253,8 @@ def test_rows_put_refuses_bad_layouts(lib):
     assert lib.kv_pool_create(ctypes.byref(d), ctypes.byref(h)) == 0
     assert lib.kv_rows_put(h, ctypes.byref(_layout(R=0)), 0x1000, 0x2000, None) == binding.KV_E_ARG
     assert lib.kv_rows_put(h, ctypes.byref(_layout()), None, 0x2000, None) == binding.KV_E_ARG
+    assert lib.kv_rows_put(h, ctypes.byref(_layout()), 0x1008, 0x2000, None) == binding.KV_E_ARG   # misaligned rows
+    assert lib.kv_rows_put(h, ctypes.byref(_layout()), 0x1000, 0x2004, None) == binding.KV_E_ARG
     assert lib.kv_rows_put(h, ctypes.byref(_layout(ring=1, R=65, max_len=300)), 0x1000, 0x2000, None) == binding.KV_E_ARG
     assert lib.kv_rows_put(None, ctypes.byref(_layout()), 0x1000, 0x2000, None) == binding.KV_E_ARG
     lib.kv_pool_destroy(h)
@@ -308,5 +312,6 @@ def test_decode_put_refuses_before_launch(lib):
     assert f(h, ctypes.byref(_layout(R=2)), ctypes.byref(_args()), 0x90000, 0xA0000, None) == binding.KV_E_ARG
     assert f(h, ctypes.byref(_layout()), ctypes.byref(_args()), None, 0xA0000, None) == binding.KV_E_ARG
     assert f(h, ctypes.byref(_layout()), ctypes.byref(_args(Hq=12)), 0x90000, 0xA0000, None) == binding.KV_E_SHAPE
+    assert f(h, ctypes.byref(_layout()), ctypes.byref(_args()), 0x90008, 0xA0000, None) == binding.KV_E_ARG   # misaligned
     assert lib.kv_last_error()
     lib.kv_pool_destroy(h)
