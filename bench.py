@@ -39,7 +39,9 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    # 100 steps (about 30 ms): the first 10-15 ms of sustained load run through a clock transient
+    # (part kernel 320-370 us against about 300 us after it)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--quick", action="store_true", help="skip the side measurements")
     ap.add_argument("--fixed-length", type=int, default=None, help="all 12 streams at this length")
