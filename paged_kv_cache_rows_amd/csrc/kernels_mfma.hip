@@ -150,7 +150,7 @@ MfmaPlan mfma_plan(int D, int G, int R, int S, int Hkv, int P, int max_seq_len, 
     int64_t chunk = ((int64_t)span * groups + target - 1) / target;
     chunk = (chunk + kt - 1) / kt * kt;
     if (chunk < lo) chunk = lo;
-    if (chunk > std::min<int64_t>(hi, 64 * kt)) chunk = std::min<int64_t>(hi, 64 * kt);
+    if (chunk > hi) chunk = hi;
     p.chunk = (int)chunk;
     return p;
 }
