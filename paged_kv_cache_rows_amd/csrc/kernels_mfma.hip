@@ -112,15 +112,17 @@ MfmaPlan mfma_plan(int D, int G, int R, int S, int Hkv, int P, int max_seq_len, 
     // table from memory per key piece); none if even the shortest does not fit
     int64_t hi = ((int64_t)(MfmaGeom<128>::TC - 2) * P - kt) / kt * kt;
     if (hi < lo) hi = (int64_t)1 << 40;
-    if (nq < 256) {
-        // Verify windows: every row sees about the same keys, so all workgroups of the call do
+    if ((int64_t)R * 8 <= span) {
+        // The rows span at most an eighth of the keys (every verify window; a prompt chunk far
+        // into its stream): every row sees about the same keys, so all workgroups of the call do
         // the same work, and one of them fills a CU (137 KB of LDS at d 128; 4 waves of more
         // than 256 registers at d 512): the call runs in rounds of 256 workgroups.  Take the
         // chunk that minimises rounds x (time of one workgroup), a workgroup costing its K/V
         // bytes at an even share of about 85 % of HBM plus about 5 us of start-up and drain
         // (both measured on the 4-stream verify).  A round left nearly empty by the chunk
         // count doubles the time: 4 streams x 36k keys in 9 chunks of 4096 (288 workgroups)
-        // took 161 us, in 8 of 4608 (256) 112 us.
+        // took 161 us, in 8 of 4608 (256) 112 us; a 128-row chunk at 40,960 keys takes 144 us in
+        // one round against 152 us in two.
         const double us_per_key = 4.0 * D / (0.85 * 8000.0e3 / 256.0), t0 = 5.0;
         double best = 0;
         int64_t best_chunk = lo;
@@ -142,10 +144,11 @@ MfmaPlan mfma_plan(int D, int G, int R, int S, int Hkv, int P, int max_seq_len, 
         p.chunk = (int)best_chunk;
         return p;
     }
-    // Prompt-sized windows on few streams: aim at 16 waves per CU over the whole call (the
-    // causal triangle gives the query tiles unequal work, so several rounds keep the grid
-    // busy): long enough chunks to amortise the per-workgroup set-up, short enough to keep
-    // every CU busy.  The 8-wave workgroups of d 128 come half as many for the same waves.
+    // Rows spread over much of the keys (an early prompt chunk on few streams): aim at 16
+    // waves per CU over the whole call (the causal triangle gives the query tiles unequal work,
+    // so several rounds keep the grid busy): long enough chunks to amortise the per-workgroup
+    // set-up, short enough to keep every CU busy.  The 8-wave workgroups of d 128 come half as
+    // many for the same waves.
     const int64_t target = p.ks == 2 ? 512 : 1024;
     int64_t chunk = ((int64_t)span * groups + target - 1) / target;
     chunk = (chunk + kt - 1) / kt * kt;

@@ -238,11 +238,13 @@ def _splits(lib, S, R, Hkv, G, D, P, max_len, window=0):
     (12, 2, 8, 8, 128, 512, 40960, 0, 8),    # 2 rows x GQA 8 = 16 query vectors: MFMA, as above
     (1, 4, 2, 8, 512, 37, 9000, 0, 94),      # d 512: chunks of 3 tiles, 188 workgroups
     (2, 8, 8, 8, 128, 512, 3000, 100, 2),    # window of 100: its keys fit one chunk, plus the edge
+    (1, 128, 8, 4, 128, 512, 40960, 0, 4),   # a 128-row prompt chunk far into its stream: 8 tiles x 8
+                                             # heads x 4 chunks = 256 workgroups, one round
 ])
 def test_verify_splits_fill_whole_rounds(lib, S, R, Hkv, G, D, P, max_len, window, splits):
-    # A verify window gives every workgroup about the same work and one workgroup fills a CU, so
-    # the call runs in rounds of 256 workgroups: the split count must not leave a round nearly
-    # empty.
+    # Rows that span a small part of the keys (verify windows, late prompt chunks) give every
+    # workgroup about the same work and one workgroup fills a CU, so the call runs in rounds of
+    # 256 workgroups: the split count must not leave a round nearly empty.
     assert _splits(lib, S, R, Hkv, G, D, P, max_len, window) == splits
 
 
