@@ -23,6 +23,8 @@
 //  * PV: a lane owns 8 channels and every 4th key (D=128) or all 16 keys (D=512); the
 //    weights of key pairs are packed to bf16 and V pairs interleaved so PV is also dot2.
 //  * The workgroup writes an unnormalised partial (acc, m, l) per query vector.
+#include <algorithm>
+
 #include "internal.h"
 #include "device_common.h"
 
@@ -45,10 +47,12 @@ struct ValuGeom {
 //    8 XCDs round-robin in grid order, so piece i of every (stream, head) then lands on XCD
 //    i mod 8 and every XCD reads the same number of bytes (measured: 8, 16, 24 or 32 pieces
 //    beat 10 or 12 by 5 to 10 percent on the 12-stream decode).
-//  * About two rounds of resident workgroups (1536 on 256 CUs): every split writes a partial
-//    (D + 2 floats per query vector) that the merge reads back, and that traffic, with the
-//    write-back of the dirty lines when the kernel ends, costs far more than its bytes, so
-//    fewer, longer pieces are better as long as every CU stays busy.
+//  * About 768 workgroups (three per CU), and pieces of at most about 2,560 keys (at d 128; the
+//    same bytes at d 512): every split writes a partial (D + 2 floats per query vector) that
+//    the merge reads back, which costs far more than its bytes, so fewer, longer pieces are
+//    better while every CU stays busy; past about 2,560 keys, more workgroups in flight win
+//    (part + merge: the 12-stream decode at 32k-40k keys takes 312.7 us with 16 pieces per
+//    stream, 320.0 with 8; one stream at 40k keys 39.1 us with 96 pieces, 44.2 with 192).
 //  * Pieces of at least 2 batches (short streams: a 2048-key decode at d 512 takes 12.4 us
 //    with 2-batch pieces, 15.6 us with 4 and 13.9 us with 1).
 // `span` bounds L - base over the call's streams.
@@ -56,9 +60,10 @@ ValuPlan valu_plan(int D, int NQ, int S, int Hkv, int span) {
     (void)NQ;
     ValuPlan p;
     p.align = D == 512 ? ValuGeom<512>::NB : ValuGeom<128>::NB;
-    const int64_t target = 1536;
     const int64_t groups = (int64_t)S * Hkv;
-    int64_t n = (target + groups - 1) / groups;
+    int64_t n = (768 + groups - 1) / groups;
+    const int64_t piece_keys = 2560 * 128 / D;
+    n = std::max<int64_t>(n, ((int64_t)span + piece_keys - 1) / piece_keys);
     if (n >= 8) n = (n + 7) / 8 * 8;
     const int64_t most = ((int64_t)span + 2 * p.align - 1) / (2 * p.align);
     if (n > most) n = most;
