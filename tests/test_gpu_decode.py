@@ -191,6 +191,27 @@ def test_sliding_window_ring_layer(R):
     assert_close(out, oracle_from_history(ks, vs, q, c.lengths, W), f"ring R={R}")
 
 
+@pytest.mark.parametrize("S,L", [(40, 3000), (100, 1500)])
+def test_decode_many_streams_few_pieces(S, L):
+    # many (stream, head) groups: the plan gives each stream 3 pieces (not a multiple of 8) or a
+    # single one; sampled streams against the oracle, and a second page order gives the same bytes
+    lengths = [L - 13 * (i % 7) for i in range(S)]
+    w = workloads.Workload(name="many", streams=S, kv_heads=8, group=8, head_dim=128, page_size=64,
+                           rows=1, lengths=lengths, spare_frac=0.05, seed=17)
+    say(f"decode {S} streams at about {L} keys")
+    c = staging.make_cache(w, order=workloads.free_order(w.pool_pages, 501))
+    ks, vs = workloads.kv_history(w, device="cuda")
+    staging.write_history(c, ks, vs)
+    q = workloads.queries(w, device="cuda")
+    out = attend("decode", c, q)
+    kb, vb = pool_bits(c)
+    for s in (0, S // 2, S - 1):
+        assert_close(out[s:s + 1], oracle_for(c, q, streams=[s], kbits=kb, vbits=vb), f"stream {s} of {S}")
+    c2 = staging.make_cache(w, order=workloads.free_order(w.pool_pages, 502))
+    staging.write_history(c2, ks, vs)
+    assert torch.equal(out.view(torch.int16), attend("decode", c2, q).view(torch.int16))
+
+
 # ----------------------------------------------------------------------------- full-size decode
 def test_batched_decode_full_size_sampled_streams():
     w = workloads.batched_decode()
