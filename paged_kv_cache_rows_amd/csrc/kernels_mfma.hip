@@ -270,6 +270,11 @@ __global__ __launch_bounds__(256 * KS) void part_mfma_kernel(const PartArgs a) {
         }
     }
 
+    // a wave whose query columns all lie past the tile's vectors (a partly filled tile: 4 rows
+    // x GQA 8 leaves waves 2 and 3 without columns) stages its share and passes every barrier,
+    // but computes nothing
+    const bool wave_live = v0 + wave * QW * 16 < NQ;
+
     const int P = a.P;
     const int kt_first = (kbeg / KT) * KT;
     const int nt = (kend - kt_first + KT - 1) / KT;     // KT-key sub-tiles
@@ -420,7 +425,7 @@ __global__ __launch_bounds__(256 * KS) void part_mfma_kernel(const PartArgs a) {
     // fragment feeds QW MFMAs (a padded step past the split computes nothing)
     auto qk = [&](int it, int buf, f32x4_t (&sacc)[QW][NB]) {
         const int tb = kt_first + (it * KS + ksub) * KT;          // sub-tile this wave computes
-        if (tb >= kend) return;
+        if (tb >= kend || !wave_live) return;
         const uint16_t *const k_lds = k_st0 + buf * KBUF;
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
@@ -438,7 +443,7 @@ __global__ __launch_bounds__(256 * KS) void part_mfma_kernel(const PartArgs a) {
     // buffer buf
     auto smpv = [&](int it, int buf, f32x4_t (&sacc)[QW][NB]) {
         const int tb = kt_first + (it * KS + ksub) * KT;
-        if (tb >= kend) return;
+        if (tb >= kend || !wave_live) return;
         const uint2 *const vt_lds = vt_st0 + buf * VBUF;
         const bool full = tb >= kbeg && tb + KT <= kend && tb + KT - 1 <= hi_full && tb >= lo_full;
         bf16x8_t pf[QW][NPM];
