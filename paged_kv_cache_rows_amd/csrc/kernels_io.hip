@@ -93,14 +93,15 @@ hipError_t launch_rows_put(const RowsArgs &a, hipStream_t st) {
     return hipGetLastError();
 }
 
-// One wave per (stream, row, query head) and slice of up to 128 channels (D / 128 waves at
-// D = 512, so that no lane walks every split alone).  Lane = (split group sg, channel block cb):
+// One wave per (stream, row, query head) and slice of channels (128 at D = 128; 64 at D = 512,
+// i.e. 8 waves, so that a lane walks few splits: the d 512 verify has about 100).  Lane =
+// (split group sg, channel block cb):
 // it owns channels [8 cb, 8 cb + 8) of its slice for the splits i = sg, sg + SG, ...; the split
 // groups are summed at the end in a fixed order, so the result depends only on the partials,
 // not on timing.
 template <int D>
 __global__ __launch_bounds__(64) void merge_kernel(const MergeArgs a) {
-    constexpr int CW = D > 128 ? 128 : D;   // channels per wave
+    constexpr int CW = D > 128 ? 64 : D;    // channels per wave
     constexpr int NCW = D / CW;             // waves per (stream, row, query head)
     constexpr int CB = CW / 8;              // channel blocks of 8
     constexpr int SG = 64 / CB;             // split groups
@@ -199,13 +200,10 @@ __global__ __launch_bounds__(64) void merge_kernel(const MergeArgs a) {
         }
     }
     // sum the split groups (lanes cb, cb + CB, ...) and the denominators (lanes 0, CB, ...)
-    if (SG > 1) {
 #pragma unroll
-        for (int c = 0; c < 8; ++c) {
-            num[c] = num[c] + __shfl_xor(num[c], 16);
-            if (SG > 2) num[c] = num[c] + __shfl_xor(num[c], 32);
-        }
-    }
+    for (int d = CB; d < 64; d *= 2)
+#pragma unroll
+        for (int c = 0; c < 8; ++c) num[c] = num[c] + __shfl_xor(num[c], d);
     den = wave_sum(den);
     if (sg == 0) {
         const float inv = den > 0.f ? 1.0f / den : 0.f;
@@ -221,7 +219,7 @@ hipError_t launch_merge(const MergeArgs &a, hipStream_t st) {
     if (blocks == 0) return hipSuccess;
     switch (a.D) {
         case 128: hipLaunchKernelGGL(merge_kernel<128>, dim3(blocks), dim3(64), 0, st, a); break;
-        case 512: hipLaunchKernelGGL(merge_kernel<512>, dim3(blocks * 4), dim3(64), 0, st, a); break;
+        case 512: hipLaunchKernelGGL(merge_kernel<512>, dim3(blocks * 8), dim3(64), 0, st, a); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
