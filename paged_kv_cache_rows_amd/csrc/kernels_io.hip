@@ -93,15 +93,14 @@ hipError_t launch_rows_put(const RowsArgs &a, hipStream_t st) {
     return hipGetLastError();
 }
 
-// One wave per (stream, row, query head) and slice of channels (128 at D = 128; 64 at D = 512,
-// i.e. 8 waves, so that a lane walks few splits: the d 512 verify has about 100).  Lane =
-// (split group sg, channel block cb):
+// One wave per (stream, row, query head) and slice of CW channels: 128 at D = 128 with up to
+// 16 splits, else 64 (so that a lane walks few splits: a d 512 verify has about 100, a long
+// single-stream decode about 100 as well).  Lane = (split group sg, channel block cb):
 // it owns channels [8 cb, 8 cb + 8) of its slice for the splits i = sg, sg + SG, ...; the split
 // groups are summed at the end in a fixed order, so the result depends only on the partials,
 // not on timing.
-template <int D>
+template <int D, int CW>
 __global__ __launch_bounds__(64) void merge_kernel(const MergeArgs a) {
-    constexpr int CW = D > 128 ? 64 : D;    // channels per wave
     constexpr int NCW = D / CW;             // waves per (stream, row, query head)
     constexpr int CB = CW / 8;              // channel blocks of 8
     constexpr int SG = 64 / CB;             // split groups
@@ -217,11 +216,14 @@ __global__ __launch_bounds__(64) void merge_kernel(const MergeArgs a) {
 hipError_t launch_merge(const MergeArgs &a, hipStream_t st) {
     const int blocks = a.S * a.R * a.Hq;
     if (blocks == 0) return hipSuccess;
-    switch (a.D) {
-        case 128: hipLaunchKernelGGL(merge_kernel<128>, dim3(blocks), dim3(64), 0, st, a); break;
-        case 512: hipLaunchKernelGGL(merge_kernel<512>, dim3(blocks * 8), dim3(64), 0, st, a); break;
-        default: return hipErrorInvalidValue;
-    }
+    if (a.D == 128 && a.n_splits <= 16)
+        hipLaunchKernelGGL((merge_kernel<128, 128>), dim3(blocks), dim3(64), 0, st, a);
+    else if (a.D == 128)
+        hipLaunchKernelGGL((merge_kernel<128, 64>), dim3(blocks * 2), dim3(64), 0, st, a);
+    else if (a.D == 512)
+        hipLaunchKernelGGL((merge_kernel<512, 64>), dim3(blocks * 8), dim3(64), 0, st, a);
+    else
+        return hipErrorInvalidValue;
     return hipGetLastError();
 }
 
