@@ -41,6 +41,17 @@ def test_random_trees_match_the_oracle(G, R, P):
     assert_close(_tree(c, q, masks), oracle_tree_for(c, q, masks), f"tree G={G} R={R} P={P}")
 
 
+@pytest.mark.parametrize("G,R", [(4, 3), (8, 4), (8, 8)])
+def test_random_trees_at_head_dim_512(G, R):
+    # the d 512 kernels: VALU at 12 query vectors, MFMA at 32 (two waves without columns) and 64
+    w = _w(group=G, rows=R, head_dim=512, kv_heads=1, page_size=37, lengths=[2000, 300, R])
+    say(f"tree d512 G={G} R={R} ({'MFMA' if R * G >= 16 else 'VALU'})")
+    c, _, _ = new_cache(w)
+    q = workloads.queries(w).cuda()
+    masks = random_tree_masks(np.random.default_rng(R * 100 + G + 512), w.streams, R)
+    assert_close(_tree(c, q, masks), oracle_tree_for(c, q, masks), f"tree d512 G={G} R={R}")
+
+
 @pytest.mark.parametrize("G,R", [(4, 3), (8, 8)])
 def test_chain_masks_equal_plain_verify_bytes(G, R):
     w = _w(group=G, rows=R)
