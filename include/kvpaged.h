@@ -131,10 +131,24 @@ kv_status kv_page_lease(kv_pool *pool, int32_t stream, int32_t n, int32_t *page_
 enum { KV_LEASE_QUEUE = 0, KV_LEASE_CONTIGUOUS = 1 };
 kv_status kv_pool_set_lease_policy(kv_pool *pool, int32_t policy);
 
-/* Return all of a stream's pages to the back of the free queue, in the order they were leased
- * (released pages are handed out again by later leases, which the PR's model test covers).  KV_E_ARG for
- * a bad stream id.  The pages' contents are left as they are. */
+/* Give up all of a stream's pages (released pages are handed out again by later leases, which
+ * the PR's model test covers).  Each page loses one holder; the pages that no other stream
+ * holds (see kv_page_share) go to the back of the free queue, in the order the stream leased
+ * them.  KV_E_ARG for a bad stream id.  The pages' contents are left as they are. */
 kv_status kv_page_release(kv_pool *pool, int32_t stream);
+
+/* Share a prefix of one stream's pages with another (TensorFold PR #1620, opening description,
+ * Kept states bullet: a kept state is resumed and its pages reused; sharing is the form of that
+ * which copies nothing).  dst_stream, which must hold no pages, takes the first n pages of
+ * src_stream's lease list, in that order; each gains a holder and none leaves the free queue.
+ * Later leases append to dst_stream's list as usual, and a page returns to the free queue only
+ * when its last holder releases it.  Both streams' tables then point at the same pages for the
+ * shared prefix, and a row written into a shared page is seen by every holder: share only pages
+ * that no holder writes again (the full pages of a common prefix) and give a partly filled last
+ * page its own copy (kv_page_lease + kv_pages_copy).  Errors: KV_E_ARG for bad stream ids,
+ * src_stream == dst_stream, n outside [0, pages src_stream holds], or a dst_stream that holds
+ * pages.  Thread-safe per pool. */
+kv_status kv_page_share(kv_pool *pool, int32_t src_stream, int32_t dst_stream, int32_t n);
 
 /* Number of free pages. */
 kv_status kv_pool_free_count(const kv_pool *pool, int32_t *out);

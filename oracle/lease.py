@@ -10,6 +10,11 @@ so this library fixes one and the model states it:
     the stream's page list.  If fewer than n are free it fails and changes nothing.
   * release(stream) appends the stream's pages to the back of the queue in the order they
     were leased, and empties the stream's list.
+  * share(src, dst, n): dst, holding nothing, takes src's first n pages in src's order
+    without touching the queue.  A page is then held by several streams; release(stream)
+    returns only the pages no other stream still holds, in the releasing stream's order.
+    (The Kept states bullet resumes a kept state and reuses its pages; sharing the full pages of
+    a common prefix is the form of that which copies nothing.)
 
 A second lease policy, "contiguous", follows the first review of the same PR (the full layers
 could keep a contiguous cache until the pool needs the room).  It hands out ids by the first
@@ -23,7 +28,9 @@ of these that applies, and removes them from the queue wherever they sit:
 
 Pins: tests/test_oracle_pins.py checks, against brute-force bookkeeping with sets, that after
 any random sequence of leases and releases the leased lists and the free list partition
-range(N), no id is leased twice, failed leases change nothing, and hand-out follows the queue.
+range(N), no id is leased twice, failed leases change nothing, and hand-out follows the queue;
+with shares, that the free list and the union of the leased lists partition range(N), that a
+page is free exactly when no list holds it, and a hand-worked sequence of shares and releases.
 The contiguous policy is pinned by a hand-worked sequence (tests/golden/contiguous_leases.json)
 that reaches each step and the tie rule, and by properties of random sequences: the same
 partition, and that every lease is one run of adjacent ids whenever the free set has one.
@@ -89,11 +96,23 @@ class LeaseModel:
         self.leased[stream].extend(got)
         return got
 
+    def holders(self, page: int) -> int:
+        """Number of streams whose list holds the page."""
+        return sum(page in lst for lst in self.leased)
+
+    def share(self, src: int, dst: int, n: int):
+        if not (0 <= src < len(self.leased) and 0 <= dst < len(self.leased)) or src == dst:
+            raise ValueError("bad streams")
+        if not 0 <= n <= len(self.leased[src]) or self.leased[dst]:
+            raise ValueError("bad count, or dst holds pages")
+        self.leased[dst] = list(self.leased[src][:n])
+
     def release(self, stream: int):
         if not (0 <= stream < len(self.leased)):
             raise ValueError("bad stream")
-        self.free.extend(self.leased[stream])
+        mine = self.leased[stream]
         self.leased[stream] = []
+        self.free.extend(i for i in mine if self.holders(i) == 0)
 
     @property
     def free_count(self) -> int:

@@ -25,7 +25,8 @@ STATUS_NAMES = {0: "KV_OK", -1: "KV_E_ARG", -2: "KV_E_SHAPE", -3: "KV_E_NO_PAGES
                 -4: "KV_E_WORKSPACE", -5: "KV_E_DEVICE"}
 
 # The entry points include/kvpaged.h declares (checked against the built library's exports).
-EXPORTS = ("kv_pool_create", "kv_pool_destroy", "kv_page_lease", "kv_page_release", "kv_pool_set_lease_policy",
+EXPORTS = ("kv_pool_create", "kv_pool_destroy", "kv_page_lease", "kv_page_release", "kv_page_share",
+           "kv_pool_set_lease_policy",
            "kv_pool_free_count", "kv_stream_pages", "kv_rows_put", "kv_pages_copy", "paged_attn_workspace_size",
            "paged_attn_decode", "paged_attn_decode_put", "paged_attn_verify", "paged_attn_verify_tree",
            "paged_attn_prefill",
@@ -73,6 +74,7 @@ def load(path: str = LIB_PATH):
         "kv_pool_destroy": [c_void_p],
         "kv_page_lease": [c_void_p, c_int32, c_int32, i32p],
         "kv_page_release": [c_void_p, c_int32],
+        "kv_page_share": [c_void_p, c_int32, c_int32, c_int32],
         "kv_pool_set_lease_policy": [c_void_p, c_int32],
         "kv_pool_free_count": [c_void_p, i32p],
         "kv_stream_pages": [c_void_p, c_int32, i32p, c_int32, i32p],
@@ -169,6 +171,10 @@ class Pool:
 
     def release(self, stream: int):
         _check(load().kv_page_release(self.handle, stream))
+
+    def share(self, src_stream: int, dst_stream: int, n: int):
+        """kv_page_share: dst_stream (holding no pages) takes src_stream's first n pages."""
+        _check(load().kv_page_share(self.handle, src_stream, dst_stream, n))
 
     def free_count(self) -> int:
         n = c_int32()

@@ -23,6 +23,7 @@ struct kv_pool {
     mutable std::mutex mu;
     std::deque<int32_t> free_q;
     std::vector<char> is_free;       // is_free[id]: id is in free_q
+    std::vector<int32_t> holders;    // streams whose lease list holds id (0 for a free page)
     int32_t policy = KV_LEASE_QUEUE;
     std::vector<std::vector<int32_t>> leased;
 };
@@ -332,6 +333,7 @@ kv_status kv_pool_create(const kv_pool_desc *d, kv_pool **out) {
     p->v_pages = static_cast<uint16_t *>(d->v_pages);
     p->free_q.assign(order.begin(), order.end());
     p->is_free.assign(d->num_pages, 1);
+    p->holders.assign(d->num_pages, 0);
     p->leased.assign(d->max_streams, {});
     *out = p;
     return ok();
@@ -358,6 +360,7 @@ kv_status kv_page_lease(kv_pool *pool, int32_t stream, int32_t n, int32_t *ids) 
             ids[i] = pool->free_q.front();
             pool->free_q.pop_front();
             pool->is_free[ids[i]] = 0;
+            pool->holders[ids[i]] = 1;
             lst.push_back(ids[i]);
         }
         return ok();
@@ -366,6 +369,7 @@ kv_status kv_page_lease(kv_pool *pool, int32_t stream, int32_t n, int32_t *ids) 
     for (int i = 0; i < n; ++i) {
         ids[i] = got[i];
         pool->is_free[got[i]] = 0;
+        pool->holders[got[i]] = 1;
         lst.push_back(got[i]);
     }
     auto &q = pool->free_q;
@@ -389,10 +393,30 @@ kv_status kv_page_release(kv_pool *pool, int32_t stream) {
         return fail(KV_E_ARG, "kv_page_release: stream %d outside [0, %d)", stream, pool->max_streams);
     auto &lst = pool->leased[stream];
     for (int32_t id : lst) {
+        if (--pool->holders[id] > 0) continue;     // another stream still holds it
         pool->free_q.push_back(id);
         pool->is_free[id] = 1;
     }
     lst.clear();
+    return ok();
+}
+
+kv_status kv_page_share(kv_pool *pool, int32_t src_stream, int32_t dst_stream, int32_t n) {
+    if (!pool) return fail(KV_E_ARG, "kv_page_share: pool is null");
+    std::lock_guard<std::mutex> lk(pool->mu);
+    if (src_stream < 0 || src_stream >= pool->max_streams || dst_stream < 0 || dst_stream >= pool->max_streams)
+        return fail(KV_E_ARG, "kv_page_share: stream %d or %d outside [0, %d)", src_stream, dst_stream,
+                    pool->max_streams);
+    if (src_stream == dst_stream) return fail(KV_E_ARG, "kv_page_share: a stream cannot share with itself");
+    const auto &src = pool->leased[src_stream];
+    auto &dst = pool->leased[dst_stream];
+    if (n < 0 || (size_t)n > src.size())
+        return fail(KV_E_ARG, "kv_page_share: n %d outside [0, %zu]", n, src.size());
+    if (!dst.empty()) return fail(KV_E_ARG, "kv_page_share: stream %d already holds pages", dst_stream);
+    for (int32_t i = 0; i < n; ++i) {
+        dst.push_back(src[i]);
+        ++pool->holders[src[i]];
+    }
     return ok();
 }
 

@@ -155,6 +155,55 @@ def test_leases_match_the_oracle_model(lib, seed):
     lib.kv_pool_destroy(h)
 
 
+@pytest.mark.parametrize("seed", range(4))
+def test_shares_match_the_oracle_model(lib, seed):
+    # leases, releases and shares (valid and refused) under both policies, library against model
+    rng = random.Random(100 + seed)
+    N, S = 48, 6
+    st, h, keep = _create(lib, num_pages=N, streams=S)
+    assert st == 0
+    model = oracle.LeaseModel(N, S)
+    buf = (ctypes.c_int32 * N)()
+    for _ in range(300):
+        s = rng.randrange(S)
+        if rng.random() < 0.05:
+            pol = rng.choice(["queue", "contiguous"])
+            assert lib.kv_pool_set_lease_policy(
+                h, binding.KV_LEASE_CONTIGUOUS if pol == "contiguous" else binding.KV_LEASE_QUEUE) == 0
+            model.set_policy(pol)
+        r = rng.random()
+        if r < 0.45:
+            n = rng.randrange(0, 8)
+            st = lib.kv_page_lease(h, s, n, buf)
+            try:
+                want = model.lease(s, n)
+            except oracle.NoPages:
+                assert st == binding.KV_E_NO_PAGES
+            else:
+                assert st == 0 and list(buf[:n]) == want
+        elif r < 0.75:
+            d = rng.randrange(S)
+            n = rng.randrange(0, len(model.leased[s]) + 2)
+            st = lib.kv_page_share(h, s, d, n)
+            try:
+                model.share(s, d, n)
+            except ValueError:
+                assert st == binding.KV_E_ARG
+            else:
+                assert st == 0
+        else:
+            assert lib.kv_page_release(h, s) == 0
+            model.release(s)
+        cnt = ctypes.c_int32()
+        lib.kv_pool_free_count(h, ctypes.byref(cnt))
+        assert cnt.value == model.free_count
+        for t in range(S):
+            got_n = ctypes.c_int32()
+            assert lib.kv_stream_pages(h, t, buf, N, ctypes.byref(got_n)) == 0
+            assert list(buf[:got_n.value]) == model.leased[t]
+    lib.kv_pool_destroy(h)
+
+
 def _layout(S=1, R=1, stride=8, max_len=300, ring=0):
     # Device pointers are never dereferenced by the refusals tested here.
     return binding.Layout(S, R, 0x30000, stride, 0x40000, max_len, ring)

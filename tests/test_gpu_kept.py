@@ -7,6 +7,8 @@ states bullet; the model test's "a kept state's resume and reused pages").
   for byte, after the original has moved on; and both match the oracle.
 * Released pages handed to another stream still hold the old stream's rows; attention over the
   new stream never reads them (stale, finite data in unused slots must not leak either).
+* A prefix shared between two streams (kv_page_share) serves both, and outlives its first
+  holder: its pages are not handed out again while the second still holds them.
 """
 import numpy as np
 import pytest
@@ -102,6 +104,63 @@ def test_released_pages_reused_by_another_stream_leak_nothing():
     last = ids[(611 - 1) // 64]
     assert not (kb[last, :, 611 % 64:] == workloads.NAN_BITS).all()     # stale rows really are there
     assert_close(out, oracle_from_history(ks1, vs1, q, [611]), "reused pages")
+
+
+def test_shared_prefix_serves_both_streams_and_outlives_its_first_holder():
+    # stream 0 writes 700 rows; stream 1 shares its 10 full pages (640 rows), gives the partly
+    # filled 11th page its own copy, and continues from row 660 with rows of its own
+    P = 64
+    w = workloads.Workload(name="share", streams=3, kv_heads=2, group=4, head_dim=128, page_size=P, rows=1,
+                           lengths=[700, 860, 1], spare_frac=0.0, min_spares=0, seed=53)
+    ks, vs = workloads.kv_history(w)
+    pool = binding.Pool(40, P, 2, 128, max_streams=3)
+    dev = pool.k_pages.device
+
+    def table_of(ids):
+        t = torch.full((1, 16), -1, dtype=torch.int32, device=dev)
+        t[0, :len(ids)] = torch.tensor(ids, dtype=torch.int32)
+        return t
+
+    def put(table, rows_k, rows_v, lo, hi):
+        binding.rows_put(pool, table, torch.tensor([hi], dtype=torch.int32, device=dev),
+                         rows_k[lo:hi][None].contiguous().to(dev), rows_v[lo:hi][None].contiguous().to(dev), hi)
+
+    ids0 = pool.lease(0, 11)
+    t0 = table_of(ids0)
+    put(t0, ks[0], vs[0], 0, 700)
+    pool.share(0, 1, 10)
+    own = pool.lease(1, 4)
+    binding.pages_copy(pool, torch.tensor([ids0[10]], dtype=torch.int32, device=dev),
+                       torch.tensor([own[0]], dtype=torch.int32, device=dev))
+    ids1 = pool.stream_pages(1)
+    assert ids1 == ids0[:10] + own
+    t1 = table_of(ids1)
+    put(t1, ks[1], vs[1], 660, 860)
+    hist_k = [ks[0][:700], torch.cat([ks[0][:660], ks[1][660:860]])]
+    hist_v = [vs[0][:700], torch.cat([vs[0][:660], vs[1][660:860]])]
+    q = workloads.normal_bf16((2, 1, w.q_heads, 128), 63).to(dev)
+    out0 = binding.decode(pool, q[0:1].contiguous(), t0, torch.tensor([700], dtype=torch.int32, device=dev), 700)
+    out1 = binding.decode(pool, q[1:2].contiguous(), t1, torch.tensor([860], dtype=torch.int32, device=dev), 860)
+    torch.cuda.synchronize()
+    ref = oracle_from_history(hist_k, hist_v, q, [700, 860])
+    assert_close(out0, ref[0:1], "stream 0 through its own pages")
+    assert_close(out1, ref[1:2], "stream 1 through the shared prefix")
+    # the first holder leaves: only its unshared 11th page returns; another stream takes every
+    # free page and overwrites it; stream 1 reads the same bytes as before
+    pool.release(0)
+    assert pool.free_count() == 40 - len(ids1)
+    ids2 = pool.lease(2, pool.free_count())
+    assert not set(ids2) & set(ids1)
+    noise = workloads.normal_bf16((len(ids2), 2, P, 128), 64).to(dev)
+    sel = torch.tensor(ids2, dtype=torch.long, device=dev)
+    pool.k_pages[sel] = noise
+    pool.v_pages[sel] = noise
+    again = binding.decode(pool, q[1:2].contiguous(), t1, torch.tensor([860], dtype=torch.int32, device=dev), 860)
+    torch.cuda.synchronize()
+    assert torch.equal(out1.view(torch.int16), again.view(torch.int16))
+    pool.release(1)
+    pool.release(2)
+    assert pool.free_count() == 40
 
 
 def dataclass_replace(w, **kw):

@@ -304,6 +304,81 @@ def test_lease_model_partitions_the_pool():
     assert list(m2.free)[-3:] == order[:3]
 
 
+def _share_sequence(model_cls=None):
+    """The hand-worked share/release sequence: True when every step gives the derived lists."""
+    m = (model_cls or oracle.LeaseModel)(8, 3)
+    ok = m.lease(0, 4) == [0, 1, 2, 3]
+    m.share(0, 1, 3)
+    ok &= m.leased[1] == [0, 1, 2] and list(m.free) == [4, 5, 6, 7]
+    ok &= m.lease(1, 2) == [4, 5]
+    m.release(0)
+    ok &= list(m.free) == [6, 7, 3]
+    m.release(1)
+    ok &= list(m.free) == [6, 7, 3, 0, 1, 2, 4, 5]
+    return bool(ok and m.lease(2, 3) == [6, 7, 3])
+
+
+class _ReleaseFreesShared(oracle.LeaseModel):
+    """Planted mistake: a release returns every page of the stream, held elsewhere or not."""
+    def release(self, stream):
+        self.free.extend(self.leased[stream])
+        self.leased[stream] = []
+
+
+def test_planted_share_mistake_turns_the_share_sequence_red():
+    assert _share_sequence()
+    assert not _share_sequence(_ReleaseFreesShared)
+
+
+def test_shared_pages_follow_the_hand_worked_sequence():
+    # 8 pages in identity order, 3 streams; each expected list is derived from the rules:
+    m = oracle.LeaseModel(8, 3)
+    assert m.lease(0, 4) == [0, 1, 2, 3]           # queue front
+    m.share(0, 1, 3)                               # stream 1 takes stream 0's first 3 pages
+    assert m.leased[1] == [0, 1, 2] and list(m.free) == [4, 5, 6, 7]
+    assert m.lease(1, 2) == [4, 5]                 # its own pages follow the shared ones
+    assert m.leased[1] == [0, 1, 2, 4, 5]
+    m.release(0)                                   # 0, 1, 2 are still held by stream 1: only 3 returns
+    assert list(m.free) == [6, 7, 3] and [m.holders(i) for i in range(8)] == [1, 1, 1, 0, 1, 1, 0, 0]
+    m.release(1)                                   # the last holder: all of stream 1's pages, in its order
+    assert list(m.free) == [6, 7, 3, 0, 1, 2, 4, 5]
+    assert m.lease(2, 3) == [6, 7, 3]
+    with pytest.raises(ValueError):
+        m.share(2, 2, 1)                           # not with itself
+    m.share(2, 0, 2)
+    with pytest.raises(ValueError):
+        m.share(2, 0, 1)                           # stream 0 already holds pages
+    with pytest.raises(ValueError):
+        m.share(2, 1, 4)                           # more than stream 2 holds
+
+
+def test_shared_pages_partition_the_pool():
+    rng = random.Random(23)
+    N, S = 40, 6
+    m = oracle.LeaseModel(N, S)
+    for _ in range(600):
+        s = rng.randrange(S)
+        r = rng.random()
+        if r < 0.5:
+            try:
+                m.lease(s, rng.randrange(0, 8))
+            except oracle.NoPages:
+                pass
+        elif r < 0.75:
+            empty = [d for d in range(S) if not m.leased[d] and d != s]
+            if empty:
+                m.share(s, rng.choice(empty), rng.randrange(0, len(m.leased[s]) + 1))
+        else:
+            m.release(s)
+        for lst in m.leased:
+            assert len(set(lst)) == len(lst)                                   # no page twice in a list
+        held = set(p for lst in m.leased for p in lst)
+        free = list(m.free)
+        assert len(set(free)) == len(free) and not held & set(free)           # free pages are not held
+        assert sorted(held | set(free)) == list(range(N))                      # nothing lost
+        assert all((m.holders(p) == 0) == (p in set(free)) for p in range(N))
+
+
 # ----------------------------------------------------------------------------- planted mistakes
 def _pins_pass():
     try:
