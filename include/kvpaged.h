@@ -16,11 +16,12 @@
  *     reports a failed launch); kv_last_error() gives the text, per calling thread.
  *   - All device buffers (pages, queries, outputs, new rows, tables, lengths, workspace) are
  *     allocated and owned by the caller and must outlive the calls that use them.  The library
- *     owns only host metadata (the pool's free list and per-stream lease lists) and allocates
- *     no device memory.
+ *     owns only host metadata (the pool's free list, per-stream lease lists and the number of
+ *     streams holding each page) and allocates no device memory.
  *   - `hip_stream` is a hipStream_t (NULL = the legacy default stream).  Device work is
  *     enqueued on it asynchronously, in the order of the calls.
- *   - bf16 means IEEE binary32 truncated to its high 16 bits (raw uint16 storage).
+ *   - bf16 is the format of the high 16 bits of an IEEE binary32 (raw uint16 storage); outputs
+ *     are rounded to it to nearest even.
  *   - Table contents and device lengths are trusted on the hot path; with the environment
  *     variable KVP_CHECK=1 every call copies them to the host first (synchronously) and refuses
  *     bad ones with KV_E_ARG.  Without it, a page id outside [0, num_pages) is never
