@@ -52,7 +52,9 @@ def attend_stream(q, k_lin, v_lin, rows: int, window: int = 0, scale=None, lengt
     """One stream: q [R][Hq][D] float64, k_lin/v_lin [L][Hkv][D] float64 -> out [R][Hq][D].
 
     `length` defaults to k_lin.shape[0].  k_lin may start at a later position than 0 (a ring
-    gives only its tail): pass `first` via a tuple (array, first_position).
+    gives only its tail): pass `first` via a tuple (array, first_position).  A row whose
+    position is negative (more rows than the stream's length, e.g. a stream of length 0) sees
+    no key and gets zeros, as a tree row that sees no key does.
     """
     first = 0
     if isinstance(k_lin, tuple):
@@ -65,10 +67,12 @@ def attend_stream(q, k_lin, v_lin, rows: int, window: int = 0, scale=None, lengt
     L = first + k_lin.shape[0] if length is None else length
     if scale is None:
         scale = 1.0 / math.sqrt(D)
-    out = np.empty((R, Hq, D), dtype=np.float64)
+    out = np.zeros((R, Hq, D), dtype=np.float64)
     for r in range(R):
         p = row_position(L, R, r)
         lo, hi = visible_range(p, window)
+        if hi <= lo:
+            continue                                          # a row before the stream
         if lo < first:
             raise ValueError(f"row {r} needs key {lo}, but the cache starts at {first}")
         for kvh in range(Hkv):

@@ -56,6 +56,25 @@ def test_verify_splits_of_many_step_counts(L, P):
     assert_close(attend("verify", c, q), oracle_for(c, q), f"verify L={L} P={P}")
 
 
+@pytest.mark.parametrize("entry,R,G,D,Hkv", [("decode", 1, 8, 128, 2), ("verify", 3, 4, 128, 2),
+                                              ("verify", 8, 8, 128, 2), ("verify", 4, 8, 512, 1),
+                                              ("prefill", 100, 4, 128, 2), ("prefill", 512, 4, 128, 8)])
+def test_rows_before_the_stream_are_zeros(entry, R, G, D, Hkv):
+    # a stream of length 0 and one shorter than the call's rows: rows at negative positions see
+    # no key and come out as zeros on every path (VALU, MFMA split, MFMA direct for 512 rows),
+    # the other rows as the oracle's; the NaN workspace must not leak into them
+    lengths = [700, 0, max(1, R - 3)]
+    w = _w(group=G, rows=R, head_dim=D, kv_heads=Hkv, page_size=64, lengths=lengths, streams=3)
+    say(f"rows before the stream: {entry} R={R} G={G} D={D}")
+    c, _, _ = new_cache(w)
+    q = workloads.queries(w).cuda()
+    out = attend(entry, c, q)
+    assert torch.isfinite(out.float()).all()
+    assert (out[1].view(torch.int16) == 0).all()
+    assert (out[2, :R - lengths[2]].view(torch.int16) == 0).all()
+    assert_close(out, oracle_for(c, q), f"{entry} R={R} with short streams")
+
+
 def test_verify_is_byte_equal_under_shuffles_and_repeat():
     w = _w(lengths=[2500, 1300, 800], streams=3, page_size=512)
     q = workloads.queries(w).cuda()

@@ -352,6 +352,22 @@ def test_shared_pages_follow_the_hand_worked_sequence():
         m.share(2, 1, 4)                           # more than stream 2 holds
 
 
+def test_rows_before_the_stream_get_zeros_and_leave_the_others_alone():
+    # a call with more rows than the stream's length: rows at negative positions see no key (a
+    # stream of length 0 has only such rows); the rows at positions >= 0 are those of a call
+    # with exactly L rows
+    rng = np.random.default_rng(77)
+    Hkv, G, D, L, R = 2, 4, 16, 3, 5
+    k = rng.standard_normal((L, Hkv, D))
+    v = rng.standard_normal((L, Hkv, D))
+    q = rng.standard_normal((R, Hkv * G, D))
+    out = oracle.attend_stream(q, k, v, R, length=L)
+    assert (out[:R - L] == 0).all()
+    assert np.array_equal(out[R - L:], oracle.attend_stream(q[R - L:], k, v, L, length=L))
+    empty = oracle.attend_stream(q[:1], k[:0], v[:0], 1, length=0)
+    assert empty.shape == (1, Hkv * G, D) and (empty == 0).all()
+
+
 def test_shared_pages_partition_the_pool():
     rng = random.Random(23)
     N, S = 40, 6
