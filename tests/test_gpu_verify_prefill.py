@@ -75,6 +75,28 @@ def test_rows_before_the_stream_are_zeros(entry, R, G, D, Hkv):
     assert_close(out, oracle_for(c, q), f"{entry} R={R} with short streams")
 
 
+@pytest.mark.parametrize("entry,R,G,D", [("decode", 1, 8, 128), ("verify", 2, 4, 128), ("verify", 8, 8, 128),
+                                         ("verify", 4, 8, 512), ("prefill", 64, 4, 128)])
+def test_peaked_softmax_with_a_late_dominant_key(entry, R, G, D):
+    # K and q scaled by 6 (scores about 36 times larger), and one key near the end of stream 0
+    # set along its first query head: that row's weights are close to one-hot and the running
+    # max jumps late, after many tiles, which exercises the rescale of every path
+    w = _w(group=G, rows=R, head_dim=D, kv_heads=2 if D == 128 else 1, page_size=64,
+           lengths=[2300, 900], streams=2)
+    say(f"peaked softmax: {entry} R={R} G={G} D={D}")
+    c, _, _ = new_cache(w, history=False)
+    ks, vs = workloads.kv_history(w)
+    q = (workloads.queries(w).float() * 6).to(torch.bfloat16)
+    ks = [(k.float() * 6).to(torch.bfloat16) for k in ks]
+    p = c.lengths[0] - R - 40
+    ks[0][p, 0] = (q[0, 0, 0].float() * 2).to(torch.bfloat16)
+    staging.write_history(c, ks, vs)
+    q = q.cuda()
+    out = attend(entry, c, q)
+    assert torch.isfinite(out.float()).all()
+    assert_close(out, oracle_for(c, q), f"peaked {entry} R={R} D={D}")
+
+
 def test_verify_is_byte_equal_under_shuffles_and_repeat():
     w = _w(lengths=[2500, 1300, 800], streams=3, page_size=512)
     q = workloads.queries(w).cuda()
