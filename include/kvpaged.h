@@ -76,8 +76,9 @@ typedef struct kv_layout {
                                   of the stream's logical page i (full layers) or ring slot i
                                   (ring layers) */
     int32_t table_stride;      /* >= the entries a stream uses (ceil(L/P), or ring_pages) */
-    const int32_t *seq_len;    /* device int32 [S]: the stream's length L after this call's rows;
-                                  the call's rows sit at positions L-R .. L-1, so R <= L */
+    const int32_t *seq_len;    /* device int32 [S]: the stream's length L >= 0 after this call's
+                                  rows; the call's rows sit at positions L-R .. L-1, and rows at
+                                  negative positions (R > L) are not written and see no key */
     int32_t max_seq_len;       /* host: an upper bound of seq_len over the call (sizes grids and
                                   the workspace; a larger device length is a caller error) */
     int32_t ring_pages;        /* 0: full layer, position j lives in page table[j / P];
@@ -192,7 +193,8 @@ kv_status paged_attn_workspace_size(const kv_pool *pool, const kv_layout *lay,
 /* Paged GQA attention for one decode row per stream (R == 1) (TensorFold PR #1620, opening
  * description, Reads bullet: decode reads its keys through the page table).  For each stream s and
  * query head h: out = softmax(scale * q K^T) V over the keys the row sees (all positions
- * 0..L-1, or the newest `window`), K and V read through the stream's page table.  Computed
+ * 0..L-1, or the newest `window`), K and V read through the stream's page table; a row
+ * that sees no key (a stream of length 0) gets zeros.  Computed
  * with fp32 accumulation; the output is rounded to bf16 (nearest even).  Results depend only
  * on the logical cache, never on which physical pages hold it (bit for bit).
  * Errors: KV_E_ARG (R != 1, null or misaligned pointers, Hq not a multiple of Hkv), KV_E_SHAPE (no kernel
