@@ -366,3 +366,27 @@ def test_decode_put_refuses_before_launch(lib):
     assert f(h, ctypes.byref(_layout()), ctypes.byref(_args()), 0x90008, 0xA0000, None) == binding.KV_E_ARG   # misaligned
     assert lib.kv_last_error()
     lib.kv_pool_destroy(h)
+
+
+def test_every_call_raises_without_the_library(tmp_path):
+    # a copy of the package without its built library: the binding raises on the first call
+    # that needs the library and never falls back to another implementation
+    import shutil
+    import sys
+    import textwrap
+    shutil.copytree(os.path.join(ROOT, "paged_kv_cache_rows_amd"), tmp_path / "paged_kv_cache_rows_amd",
+                    ignore=shutil.ignore_patterns("*.so", "_build", "__pycache__"))
+    code = textwrap.dedent("""
+        from paged_kv_cache_rows_amd import binding
+        calls = (lambda: binding.Pool(8, 64, 1, 128, 1, device="cpu"), binding.abi_version, binding.load)
+        for call in calls:
+            try:
+                call()
+            except RuntimeError as e:
+                assert "is missing" in str(e), e
+            else:
+                raise SystemExit("a call ran without the library")
+        print("all raised")
+    """)
+    r = subprocess.run([sys.executable, "-c", code], cwd=tmp_path, capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0 and "all raised" in r.stdout, r.stdout + r.stderr
