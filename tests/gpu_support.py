@@ -26,7 +26,7 @@ def pool_bits(cache):
 
 
 def oracle_for(cache, q: torch.Tensor, window: int = 0, streams=None, kbits=None, vbits=None,
-               lengths=None):
+               lengths=None, scale=None):
     """Oracle output [S'][R][Hq][D] float64 for the selected streams, gathering each stream's
     linear cache from host copies of the GPU pool through the oracle's own table walk."""
     if kbits is None:
@@ -45,7 +45,7 @@ def oracle_for(cache, q: torch.Tensor, window: int = 0, streams=None, kbits=None
         else:
             kl, vl = oracle.bf16_bits_to_f64(kl), oracle.bf16_bits_to_f64(vl)
         qs = oracle.bf16_bits_to_f64(qb[s])
-        outs.append(oracle.attend_stream(qs, kl, vl, qs.shape[0], window, length=L))
+        outs.append(oracle.attend_stream(qs, kl, vl, qs.shape[0], window, scale=scale, length=L))
     return np.stack(outs)
 
 

@@ -97,6 +97,25 @@ def test_peaked_softmax_with_a_late_dominant_key(entry, R, G, D):
     assert_close(out, oracle_for(c, q), f"peaked {entry} R={R} D={D}")
 
 
+@pytest.mark.parametrize("entry,R,G,D", [("decode", 1, 8, 128), ("decode", 1, 4, 512), ("verify", 3, 4, 128),
+                                         ("verify", 8, 8, 128), ("verify", 4, 8, 512), ("prefill", 64, 4, 128),
+                                         ("prefill", 512, 4, 128)])
+@pytest.mark.parametrize("scale", [0.02, 0.25])
+def test_explicit_scale_on_every_path(entry, R, G, D, scale):
+    # a caller-given scale in place of 1/sqrt(d) (0.088 at d 128, 0.044 at d 512): flatter and
+    # sharper weights on the VALU path, the MFMA split at d 128 and 512 and the direct plan
+    Hkv = 8 if R == 512 else (2 if D == 128 else 1)
+    w = _w(group=G, rows=R, head_dim=D, kv_heads=Hkv, page_size=64, lengths=[1500, 600], streams=2)
+    say(f"scale {scale}: {entry} R={R} G={G} D={D}")
+    c, _, _ = new_cache(w)
+    q = workloads.queries(w).cuda()
+    out = attend(entry, c, q, scale=scale)
+    assert torch.isfinite(out.float()).all()
+    assert_close(out, oracle_for(c, q, scale=scale), f"{entry} R={R} D={D} scale {scale}")
+    # the scale reaches the kernels: the default gives different bytes
+    assert not torch.equal(out.view(torch.int16), attend(entry, c, q).view(torch.int16))
+
+
 def test_verify_is_byte_equal_under_shuffles_and_repeat():
     w = _w(lengths=[2500, 1300, 800], streams=3, page_size=512)
     q = workloads.queries(w).cuda()
