@@ -1,4 +1,5 @@
-"""GPU tests of a decode step captured in a HIP graph and replayed while the streams grow.
+"""GPU tests of calls captured in HIP graphs: a decode step replayed while the streams grow,
+and verify windows and prompt chunks replayed over fixed inputs.
 
 The launch grid of a call is sized from the host ceiling `max_seq_len` and every stream length
 is read from device memory, so one captured step (kv_rows_put of each stream's new row, then
@@ -13,7 +14,7 @@ eager work (updating the lengths, the new rows and the queries) runs between the
 import pytest
 import torch
 
-from gpu_support import assert_close, new_cache, oracle_from_history, say
+from gpu_support import assert_close, new_cache, oracle_for, oracle_from_history, poisoned_workspace, say
 from paged_kv_cache_rows_amd import binding, staging, workloads
 
 pytestmark = pytest.mark.gpu
@@ -81,3 +82,39 @@ def test_captured_decode_step_replays_as_streams_grow():
         assert torch.equal(got.view(torch.int16), eager.view(torch.int16)), f"replay {i} differs from eager"
         assert_close(got, oracle_from_history(ks, vs, q, lengths), f"replay {i}")
     del g
+
+
+@pytest.mark.parametrize("entry,R,G,D,Hkv", [("verify", 8, 8, 128, 2), ("verify", 3, 4, 128, 2),
+                                              ("verify", 4, 8, 512, 1), ("prefill", 64, 4, 128, 2),
+                                              ("prefill", 512, 4, 128, 8)])
+def test_captured_verify_and_prompt_calls_replay_byte_equal(entry, R, G, D, Hkv):
+    # a verify window (VALU at 3 rows x GQA 4, MFMA split with its merge otherwise) or a prompt
+    # chunk (split plan at 64 rows, direct plan at 512) captured once; before every replay the
+    # output and the workspace are refilled with NaN bytes by eager work
+    w = workloads.Workload(name="graph", streams=2, kv_heads=Hkv, group=G, head_dim=D, page_size=64,
+                           rows=R, lengths=[1500, 700], spare_frac=0.2, min_spares=2, seed=41)
+    say(f"captured {entry} R={R} G={G} D={D}")
+    c, _, _ = new_cache(w)
+    q = workloads.queries(w).cuda()
+    ws = poisoned_workspace(c, R, w.q_heads)
+    fn = {"verify": binding.verify, "prefill": binding.prefill}[entry]
+    eager = fn(c.pool, q, c.table, c.seq_len, c.max_seq_len, workspace=ws)
+    torch.cuda.synchronize()
+    out = torch.empty_like(q)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn(c.pool, q, c.table, c.seq_len, c.max_seq_len, out=out, workspace=ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn(c.pool, q, c.table, c.seq_len, c.max_seq_len, out=out, workspace=ws)
+    for i in range(STEPS):
+        out.view(torch.int16).fill_(0x7FC0)
+        ws.fill_(0xFF)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), eager.view(torch.int16)), f"replay {i} differs from eager"
+    assert_close(out, oracle_for(c, q), f"captured {entry} R={R} D={D}")
