@@ -1,5 +1,5 @@
-"""GPU tests of calls captured in HIP graphs: a decode step replayed while the streams grow,
-and verify windows and prompt chunks replayed over fixed inputs.
+"""GPU tests of calls captured in HIP graphs (a decode step replayed while the streams grow,
+verify windows and prompt chunks replayed over fixed inputs) and of calls on side streams.
 
 The launch grid of a call is sized from the host ceiling `max_seq_len` and every stream length
 is read from device memory, so one captured step (kv_rows_put of each stream's new row, then
@@ -118,3 +118,34 @@ def test_captured_verify_and_prompt_calls_replay_byte_equal(entry, R, G, D, Hkv)
         torch.cuda.synchronize()
         assert torch.equal(out.view(torch.int16), eager.view(torch.int16)), f"replay {i} differs from eager"
     assert_close(out, oracle_for(c, q), f"captured {entry} R={R} D={D}")
+
+
+def test_calls_on_two_streams_at_once_match_the_default_stream():
+    # a verify window (MFMA split and merge) and a decode (VALU) on two side streams, enqueued
+    # in turn with no synchronisation between them: the library keeps no device state of its
+    # own (every buffer is the caller's), so each equals the same call on the default stream
+    wa = workloads.Workload(name="sa", streams=2, kv_heads=2, group=8, head_dim=128, page_size=64,
+                            rows=8, lengths=[1500, 700], spare_frac=0.2, min_spares=2, seed=51)
+    wb = workloads.Workload(name="sb", streams=3, kv_heads=2, group=8, head_dim=128, page_size=37,
+                            rows=1, lengths=[900, 40, 2000], spare_frac=0.2, min_spares=2, seed=52)
+    say("verify and decode on two side streams")
+    ca, _, _ = new_cache(wa)
+    cb, _, _ = new_cache(wb)
+    qa = workloads.queries(wa).cuda()
+    qb = workloads.queries(wb).cuda()
+    ref_a = binding.verify(ca.pool, qa, ca.table, ca.seq_len, ca.max_seq_len)
+    ref_b = binding.decode(cb.pool, qb, cb.table, cb.seq_len, cb.max_seq_len)
+    wsa = poisoned_workspace(ca, wa.rows, wa.q_heads)
+    wsb = poisoned_workspace(cb, wb.rows, wb.q_heads)
+    oa, ob = torch.empty_like(qa), torch.empty_like(qb)
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    s1.wait_stream(torch.cuda.current_stream())
+    s2.wait_stream(torch.cuda.current_stream())
+    for _ in range(3):
+        with torch.cuda.stream(s1):
+            binding.verify(ca.pool, qa, ca.table, ca.seq_len, ca.max_seq_len, out=oa, workspace=wsa)
+        with torch.cuda.stream(s2):
+            binding.decode(cb.pool, qb, cb.table, cb.seq_len, cb.max_seq_len, out=ob, workspace=wsb)
+    torch.cuda.synchronize()
+    assert torch.equal(oa.view(torch.int16), ref_a.view(torch.int16))
+    assert torch.equal(ob.view(torch.int16), ref_b.view(torch.int16))
