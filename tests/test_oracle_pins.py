@@ -105,6 +105,18 @@ def test_oracle_matches_brute_force(seed):
     np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-13)
 
 
+@pytest.mark.parametrize("seed,scale", [(101, 0.02), (102, 0.3), (103, 1.7)])
+def test_oracle_matches_brute_force_at_a_given_scale(seed, scale):
+    # a caller-given scale replaces 1/sqrt(d): the oracle must use it (and not the default)
+    rng = np.random.default_rng(seed)
+    lengths = [int(rng.integers(4, 30)) for _ in range(2)]
+    q, ks, vs = _random_case(rng, 2, 3, 2, 2, 8, lengths)
+    got = oracle.attend(q, ks, vs, lengths, 0, scale=scale)
+    want = brute_attention(q.tolist(), [x.tolist() for x in ks], [x.tolist() for x in vs], lengths, 0, scale=scale)
+    np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-13)
+    assert np.abs(got - oracle.attend(q, ks, vs, lengths, 0)).max() > 1e-3
+
+
 # ----------------------------------------------------------------------------- closed forms
 def test_one_key_gives_v_exactly():
     rng = np.random.default_rng(1)
