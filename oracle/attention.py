@@ -51,20 +51,15 @@ def visible_range(p: int, window: int):
 def attend_stream(q, k_lin, v_lin, rows: int, window: int = 0, scale=None, length=None):
     """One stream: q [R][Hq][D] float64, k_lin/v_lin [L][Hkv][D] float64 -> out [R][Hq][D].
 
-    `length` defaults to k_lin.shape[0].  k_lin may start at a later position than 0 (a ring
-    gives only its tail): pass `first` via a tuple (array, first_position).  A row whose
-    position is negative (more rows than the stream's length, e.g. a stream of length 0) sees
-    no key and gets zeros, as a tree row that sees no key does.
+    `length` defaults to k_lin.shape[0]; k_lin and v_lin hold positions 0 .. length - 1.  A row
+    whose position is negative (more rows than the stream's length, e.g. a stream of length 0)
+    sees no key and gets zeros, as a tree row that sees no key does.
     """
-    first = 0
-    if isinstance(k_lin, tuple):
-        k_lin, first = k_lin
-        v_lin, _ = v_lin
     q = np.asarray(q, dtype=np.float64)
     R, Hq, D = q.shape
     Hkv = k_lin.shape[1]
     G = Hq // Hkv
-    L = first + k_lin.shape[0] if length is None else length
+    L = k_lin.shape[0] if length is None else length
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     out = np.zeros((R, Hq, D), dtype=np.float64)
@@ -73,11 +68,9 @@ def attend_stream(q, k_lin, v_lin, rows: int, window: int = 0, scale=None, lengt
         lo, hi = visible_range(p, window)
         if hi <= lo:
             continue                                          # a row before the stream
-        if lo < first:
-            raise ValueError(f"row {r} needs key {lo}, but the cache starts at {first}")
         for kvh in range(Hkv):
-            K = k_lin[lo - first:hi - first, kvh, :]          # [n][D]
-            V = v_lin[lo - first:hi - first, kvh, :]
+            K = k_lin[lo:hi, kvh, :]                          # [n][D]
+            V = v_lin[lo:hi, kvh, :]
             heads = [h for h in range(Hq) if kv_head_of(h, G) == kvh]
             Q = q[r, heads, :]                                # [G][D]
             s = (Q @ K.T) * scale                             # [G][n]
@@ -129,8 +122,8 @@ def attend_stream_tree(q, k_lin, v_lin, rows: int, masks, window: int = 0, scale
 
 
 def attend(q, k_lins, v_lins, lengths, window: int = 0, scale=None):
-    """All streams: q [S][R][Hq][D]; k_lins[s], v_lins[s] are [L_s][Hkv][D] (or (array, first)
-    tuples for ring tails).  Returns out [S][R][Hq][D] float64."""
+    """All streams: q [S][R][Hq][D]; k_lins[s], v_lins[s] are [L_s][Hkv][D].  Returns
+    out [S][R][Hq][D] float64."""
     q = np.asarray(q, dtype=np.float64)
     S, R = q.shape[:2]
     out = np.empty(q.shape, dtype=np.float64)

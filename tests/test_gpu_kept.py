@@ -15,7 +15,7 @@ import pytest
 import torch
 
 import oracle
-from gpu_support import assert_close, new_cache, oracle_for, oracle_from_history, pool_bits, say
+from gpu_support import assert_close, expected_pool, new_cache, oracle_from_history, pool_bits, say
 from paged_kv_cache_rows_amd import binding, staging, workloads
 
 pytestmark = pytest.mark.gpu
@@ -32,7 +32,9 @@ def _w(**kw):
 def test_pages_copy_bytes_equal_the_oracle_copy(P, D):
     w = _w(page_size=P, head_dim=D, lengths=[2 * P + 5, P, 3 * P])
     c, _, _ = new_cache(w)
-    kb, vb = pool_bits(c)
+    kb, vb = expected_pool(c)                               # the oracle's scatter of the history
+    gk, gv = pool_bits(c)
+    assert np.array_equal(gk, kb) and np.array_equal(gv, vb)
     rng = np.random.default_rng(P + D)
     ids = rng.permutation(w.pool_pages)
     n = w.pool_pages // 2

@@ -10,7 +10,7 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_support import assert_close, attend, oracle_for, say
+from gpu_support import assert_close, attend, oracle_for, remember, say
 from paged_kv_cache_rows_amd import binding, staging, workloads
 
 pytestmark = pytest.mark.gpu
@@ -38,7 +38,7 @@ def test_contiguous_leases_give_the_same_bytes_as_shuffled_pages(P):
         else:
             c = staging.make_cache(w, order=workloads.free_order(w.pool_pages, 7101))
         staging.write_history(c, ks, vs)
-        caches.append(c)
+        caches.append(remember(c, ks, vs))
     runs = [_runs(caches[0].table_host[s][:w.pages_for(L)]) for s, L in enumerate(w.lengths)]
     say(f"runs per stream: {runs}")
     assert min(runs) == 1 and max(runs) >= 2          # contiguous where it fits, spilled where not

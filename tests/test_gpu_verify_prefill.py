@@ -8,8 +8,8 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_support import (assert_close, attend, compare, new_cache, oracle_for, oracle_from_history,
-                         pool_bits, say)
+from gpu_support import (assert_close, attend, new_cache, oracle_for, oracle_from_history, pool_bits,
+                         remember, say)
 from paged_kv_cache_rows_amd import binding, staging, workloads
 
 pytestmark = pytest.mark.gpu
@@ -91,6 +91,7 @@ def test_peaked_softmax_with_a_late_dominant_key(entry, R, G, D):
     p = c.lengths[0] - R - 40
     ks[0][p, 0] = (q[0, 0, 0].float() * 2).to(torch.bfloat16)
     staging.write_history(c, ks, vs)
+    remember(c, ks, vs)
     q = q.cuda()
     out = attend(entry, c, q)
     assert torch.isfinite(out.float()).all()
@@ -156,7 +157,7 @@ def test_verify_sliding_window(W):
 def test_wide_head_pair_with_nan_in_unused_slots():
     w = workloads.wide_head()
     assert w.page_size == 37 and w.head_dim == 512
-    c, _, _ = new_cache(w)
+    c, ks, vs = new_cache(w)
     kb, vb = pool_bits(c)
     # the last page of each stream has unused slots, and they hold the NaN pattern
     for s, L in enumerate(c.lengths):
@@ -172,9 +173,8 @@ def test_wide_head_pair_with_nan_in_unused_slots():
     o0 = binding.decode(c.pool, q0, t0, l0, c.lengths[0])
     o1 = binding.verify(c.pool, q1, t1, l1, c.lengths[1])
     torch.cuda.synchronize()
-    assert_close(o0, oracle_for(c, q0, streams=[0], kbits=kb, vbits=vb), "wide decode L=2048")
-    c1 = dataclasses.replace(c, lengths=[c.lengths[1]], table_host=c.table_host[1:])
-    assert_close(o1, oracle_for(c1, q1, streams=[0], kbits=kb, vbits=vb), "wide verify L=9000 R=4")
+    assert_close(o0, oracle_from_history(ks[:1], vs[:1], q0, c.lengths[:1]), "wide decode L=2048")
+    assert_close(o1, oracle_from_history(ks[1:], vs[1:], q1, c.lengths[1:]), "wide verify L=9000 R=4")
 
 
 # ----------------------------------------------------------------------------- prefill
