@@ -17,7 +17,9 @@
  *   - All device buffers (pages, queries, outputs, new rows, tables, lengths, workspace) are
  *     allocated and owned by the caller and must outlive the calls that use them.  The library
  *     owns only host metadata (the pool's free list, per-stream lease lists and the number of
- *     streams holding each page) and allocates no device memory.
+ *     streams holding each page) and allocates no device memory.  The one piece of device
+ *     memory it holds is the fixed scratch array of paged_attn_decode_put_static, part of its
+ *     code object on every GPU it runs on.
  *   - `hip_stream` is a hipStream_t (NULL = the legacy default stream).  Device work is
  *     enqueued on it asynchronously, in the order of the calls.
  *   - bf16 is the format of the high 16 bits of an IEEE binary32 (raw uint16 storage); outputs
@@ -210,6 +212,22 @@ kv_status paged_attn_decode(const kv_pool *pool, const kv_layout *lay, const kv_
  * two calls.  Errors as for decode, with KV_E_ARG for a null or misaligned k_new or v_new. */
 kv_status paged_attn_decode_put(const kv_pool *pool, const kv_layout *lay, const kv_attn_args *a,
                                 const void *k_new, const void *v_new, void *hip_stream);
+
+/* paged_attn_decode_put for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation.  The split partials go to a
+ * scratch array of KV_STATIC_SCRATCH_BYTES that the library keeps in the memory of each GPU it
+ * runs on (from the first call on that GPU until the process ends); a->workspace and
+ * a->workspace_bytes are ignored, and nothing is allocated or freed.  The caller still passes
+ * every input and output.  All calls on one GPU share that GPU's array: calls that may run at
+ * the same time on one GPU (on different streams, or from different threads) race on it and
+ * must be ordered by the caller.  Nothing in the array needs to start at zero (every partial a
+ * call reads is written earlier in the same call).  Errors as for paged_attn_decode_put, and
+ * KV_E_WORKSPACE when the call needs more scratch than the array holds (the size
+ * paged_attn_workspace_size reports for the same arguments must not exceed
+ * KV_STATIC_SCRATCH_BYTES), KV_E_DEVICE if the array's address cannot be looked up. */
+#define KV_STATIC_SCRATCH_BYTES (32u << 20)
+kv_status paged_attn_decode_put_static(const kv_pool *pool, const kv_layout *lay, const kv_attn_args *a,
+                                       const void *k_new, const void *v_new, void *hip_stream);
 
 /* The same for a speculative verify window of 1 <= R <= 8 causal rows per stream (TensorFold
  * PR #2730, What this changes: the pending token plus up to seven drafts, and the window

@@ -28,7 +28,7 @@ STATUS_NAMES = {0: "KV_OK", -1: "KV_E_ARG", -2: "KV_E_SHAPE", -3: "KV_E_NO_PAGES
 EXPORTS = ("kv_pool_create", "kv_pool_destroy", "kv_page_lease", "kv_page_release", "kv_page_share",
            "kv_pool_set_lease_policy",
            "kv_pool_free_count", "kv_stream_pages", "kv_rows_put", "kv_pages_copy", "paged_attn_workspace_size",
-           "paged_attn_decode", "paged_attn_decode_put", "paged_attn_verify", "paged_attn_verify_tree",
+           "paged_attn_decode", "paged_attn_decode_put", "paged_attn_decode_put_static", "paged_attn_verify", "paged_attn_verify_tree",
            "paged_attn_prefill",
            "kv_set_part_events",
            "kv_last_error", "kv_abi_version")
@@ -83,6 +83,8 @@ def load(path: str = LIB_PATH):
         "paged_attn_workspace_size": [c_void_p, POINTER(Layout), POINTER(AttnArgs), POINTER(c_size_t)],
         "paged_attn_decode": [c_void_p, POINTER(Layout), POINTER(AttnArgs), c_void_p],
         "paged_attn_decode_put": [c_void_p, POINTER(Layout), POINTER(AttnArgs), c_void_p, c_void_p, c_void_p],
+        "paged_attn_decode_put_static": [c_void_p, POINTER(Layout), POINTER(AttnArgs), c_void_p, c_void_p,
+                                         c_void_p],
         "paged_attn_verify": [c_void_p, POINTER(Layout), POINTER(AttnArgs), c_void_p],
         "paged_attn_verify_tree": [c_void_p, POINTER(Layout), POINTER(AttnArgs), c_void_p, c_void_p],
         "paged_attn_prefill": [c_void_p, POINTER(Layout), POINTER(AttnArgs), c_void_p],
@@ -275,6 +277,35 @@ def decode_put(pool, q, table, seq_len, max_seq_len, k_new: torch.Tensor, v_new:
     _need(v_new, torch.bfloat16, "v_new", shape)
     return _attend("paged_attn_decode_put", pool, q, table, seq_len, max_seq_len,
                    extra=(_ptr(k_new), _ptr(v_new)), **kw)
+
+
+STATIC_SCRATCH_BYTES = 32 << 20     # KV_STATIC_SCRATCH_BYTES
+
+
+def decode_put_static(pool, q, table, seq_len, max_seq_len, k_new: torch.Tensor, v_new: torch.Tensor,
+                      window: int = 0, ring_pages: int = 0, scale: float = 0.0, out: torch.Tensor | None = None,
+                      stream=None):
+    """paged_attn_decode_put_static: paged_attn_decode_put with the library's own per-GPU
+    scratch in place of a workspace (no workspace is passed or allocated).  Calls that may run
+    at the same time on one GPU race on that scratch."""
+    if q.dim() != 4 or q.shape[1] != 1 or q.shape[3] != pool.head_dim:
+        raise ValueError("q must be [S][1][Hq][D]")
+    _need(q, torch.bfloat16, "q")
+    shape = (int(q.shape[0]), 1, pool.kv_heads, pool.head_dim)
+    _need(k_new, torch.bfloat16, "k_new", shape)
+    _need(v_new, torch.bfloat16, "v_new", shape)
+    if out is None:
+        if stream is not None:
+            with torch.cuda.stream(stream):
+                out = torch.empty_like(q)
+        else:
+            out = torch.empty_like(q)
+    _need(out, torch.bfloat16, "out", q.shape)
+    lay = _layout(pool, table, seq_len, 1, max_seq_len, ring_pages)
+    args = AttnArgs(_ptr(q), _ptr(out), int(q.shape[2]), float(scale), int(window), None, 0)
+    _check(load().paged_attn_decode_put_static(pool.handle, ctypes.byref(lay), ctypes.byref(args), _ptr(k_new),
+                                               _ptr(v_new), _stream_handle(stream)))
+    return out
 
 
 def verify(pool, q, table, seq_len, max_seq_len, **kw):

@@ -18,7 +18,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libkvpaged.so")
 
-SOURCES = ["api.cpp", "kernels_io.hip", "kernels_valu.hip", "kernels_mfma.hip"]
+SOURCES = ["api.cpp", "kernels_io.hip", "kernels_valu.hip", "kernels_mfma.hip", "scratch.hip"]
 ARCH = "gfx950"
 # Packed fp32 instructions are turned off for every HIP translation unit.
 FLAGS = [

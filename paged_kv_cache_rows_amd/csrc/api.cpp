@@ -534,6 +534,28 @@ kv_status paged_attn_decode_put(const kv_pool *pool, const kv_layout *lay, const
     return run_attention(pool, lay, a, hip_stream, "paged_attn_decode_put", nullptr, k_new, v_new);
 }
 
+kv_status paged_attn_decode_put_static(const kv_pool *pool, const kv_layout *lay, const kv_attn_args *a,
+                                       const void *k_new, const void *v_new, void *hip_stream) {
+    const char *who = "paged_attn_decode_put_static";
+    if (lay && lay->rows != 1) return fail(KV_E_ARG, "%s: rows %d != 1", who, lay->rows);
+    if (!k_new || !v_new) return fail(KV_E_ARG, "%s: k_new or v_new is null", who);
+    Plan p;
+    kv_status st = make_plan(pool, lay, a, &p, who);
+    if (st != KV_OK) return st;
+    const size_t need = workspace_bytes(p);
+    if (need > (size_t)KV_STATIC_SCRATCH_BYTES)
+        return fail(KV_E_WORKSPACE, "%s: the call needs %zu bytes of scratch, more than the %zu the library holds",
+                    who, need, (size_t)KV_STATIC_SCRATCH_BYTES);
+    void *ptr = nullptr;
+    size_t have = 0;
+    const hipError_t e = kvp::static_scratch(&ptr, &have);
+    if (e != hipSuccess) return fail(KV_E_DEVICE, "%s: looking up the scratch array failed: %s", who, hipGetErrorString(e));
+    kv_attn_args b = *a;
+    b.workspace = ptr;
+    b.workspace_bytes = have;
+    return run_attention(pool, lay, &b, hip_stream, who, nullptr, k_new, v_new);
+}
+
 kv_status paged_attn_verify(const kv_pool *pool, const kv_layout *lay, const kv_attn_args *a, void *hip_stream) {
     if (lay && (lay->rows < 1 || lay->rows > 8))
         return fail(KV_E_ARG, "paged_attn_verify: rows %d outside 1..8", lay->rows);

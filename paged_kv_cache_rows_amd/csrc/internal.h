@@ -105,4 +105,8 @@ hipError_t launch_part_mfma(int D, int G, const MfmaPlan &p, const PartArgs &a, 
 hipError_t launch_merge(const MergeArgs &a, hipStream_t st);
 hipError_t launch_pages_copy(const CopyArgs &a, hipStream_t st);
 
+// Device address and size of the current GPU's static scratch array (looked up on the first
+// call per GPU, with that GPU current).
+hipError_t static_scratch(void **ptr, size_t *bytes);
+
 }  // namespace kvp

@@ -390,3 +390,38 @@ def test_every_call_raises_without_the_library(tmp_path):
     """)
     r = subprocess.run([sys.executable, "-c", code], cwd=tmp_path, capture_output=True, text=True, timeout=300)
     assert r.returncode == 0 and "all raised" in r.stdout, r.stdout + r.stderr
+
+
+@host_only
+def test_decode_put_static_refuses_before_launch(lib):
+    d = binding.PoolDesc(8, 64, 4, 128, 2, 0x10000, 0x20000, None)
+    h = ctypes.c_void_p()
+    assert lib.kv_pool_create(ctypes.byref(d), ctypes.byref(h)) == 0
+    f = lib.paged_attn_decode_put_static
+    assert f(h, ctypes.byref(_layout(R=2)), ctypes.byref(_args()), 0x90000, 0xA0000, None) == binding.KV_E_ARG
+    assert f(h, ctypes.byref(_layout()), ctypes.byref(_args()), None, 0xA0000, None) == binding.KV_E_ARG
+    assert f(h, ctypes.byref(_layout()), ctypes.byref(_args(Hq=12)), 0x90000, 0xA0000, None) == binding.KV_E_SHAPE
+    lib.kv_pool_destroy(h)
+    # partials larger than the library's scratch: refused with KV_E_WORKSPACE before anything
+    # touches a device (200 streams of 64 query heads at a 40k ceiling need about 100 MB)
+    d = binding.PoolDesc(100, 512, 8, 128, 2, 0x10000, 0x20000, None)
+    assert lib.kv_pool_create(ctypes.byref(d), ctypes.byref(h)) == 0
+    big = binding.Layout(200, 1, 0x30000, 80, 0x40000, 40960, 0)
+    n = ctypes.c_size_t()
+    assert lib.paged_attn_workspace_size(h, ctypes.byref(big), ctypes.byref(_args(Hq=64)), ctypes.byref(n)) == 0
+    assert n.value > binding.STATIC_SCRATCH_BYTES
+    assert f(h, ctypes.byref(big), ctypes.byref(_args(Hq=64)), 0x90000, 0xA0000, None) == binding.KV_E_WORKSPACE
+    assert b"scratch" in lib.kv_last_error()
+    # a call that fits goes on to look up the scratch array, which needs a device: without one
+    # the lookup fails and is reported, still before any launch
+    small = binding.Layout(12, 1, 0x30000, 80, 0x40000, 40960, 0)
+    assert lib.paged_attn_workspace_size(h, ctypes.byref(small), ctypes.byref(_args(Hq=64)), ctypes.byref(n)) == 0
+    assert n.value <= binding.STATIC_SCRATCH_BYTES
+    assert f(h, ctypes.byref(small), ctypes.byref(_args(Hq=64)), 0x90000, 0xA0000, None) == binding.KV_E_DEVICE
+    lib.kv_pool_destroy(h)
+
+
+def test_static_scratch_size_matches_the_header():
+    text = open(HEADER).read()
+    m = re.search(r"#define KV_STATIC_SCRATCH_BYTES \((\d+)u << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == binding.STATIC_SCRATCH_BYTES
