@@ -17,6 +17,9 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libkvpaged.so")
+# the benchmark's HBM read probe, a library of its own (not part of the attention ABI)
+PROBE_LIB = os.path.join(HERE, "libkvprobe.so")
+PROBE_SOURCES = ["probe.hip"]
 
 SOURCES = ["api.cpp", "kernels_io.hip", "kernels_valu.hip", "kernels_mfma.hip", "scratch.hip"]
 ARCH = "gfx950"
@@ -58,23 +61,29 @@ def _compile(src: str, verbose: bool):
     return obj, report
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=min(4, len(SOURCES))) as ex:
-        results = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
-    objs = [r[0] for r in results]
-    with open(os.path.join(BUILD, "resource_usage.txt"), "w") as f:
-        for _, rep in results:
-            f.write("\n".join(rep) + ("\n" if rep else ""))
-    tmp = LIB + ".tmp"
+def _link(objs, lib: str, verbose: bool):
+    tmp = lib + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp,
            "-Wl,-rpath,/opt/rocm/lib", "-Wl,--no-undefined"]
     if verbose:
         print(" ".join(cmd), flush=True)
     p = subprocess.run(cmd, capture_output=True, text=True)
     if p.returncode != 0:
-        raise RuntimeError(f"linking failed:\n{p.stdout}\n{p.stderr}")
-    os.replace(tmp, LIB)
+        raise RuntimeError(f"linking {os.path.basename(lib)} failed:\n{p.stdout}\n{p.stderr}")
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = SOURCES + PROBE_SOURCES
+    with cf.ThreadPoolExecutor(max_workers=min(4, len(srcs))) as ex:
+        results = dict(zip(srcs, ex.map(lambda s: _compile(s, verbose), srcs)))
+    with open(os.path.join(BUILD, "resource_usage.txt"), "w") as f:
+        for src in SOURCES:
+            rep = results[src][1]
+            f.write("\n".join(rep) + ("\n" if rep else ""))
+    _link([results[s][0] for s in SOURCES], LIB, verbose)
+    _link([results[s][0] for s in PROBE_SOURCES], PROBE_LIB, verbose)
     return LIB
 
 
