@@ -74,7 +74,7 @@ __device__ __forceinline__ int vt_unit(int ch, int kg) {
 int mfma_tile_keys(int D) { return D == 512 ? MfmaGeom<512>::KT : MfmaGeom<128>::KT; }
 
 bool mfma_supported(int D, int G, int R) {
-    return (D == 128 || D == 512) && (G == 4 || G == 8) && R >= 1 && R * G >= 16;
+    return (D == 128 || D == 512) && (G == 4 || G == 8 || G == 12 || G == 16) && R >= 1 && R * G >= 16;
 }
 
 // Query-column blocks per wave, query tiles and chunk length of one call.  Everything here is
@@ -731,8 +731,12 @@ hipError_t launch_part_mfma(int D, int G, const MfmaPlan &p, const PartArgs &arg
     if (p.qw != 1 || p.ks != (D == 128 ? 2 : 1)) return hipErrorInvalidValue;
     if (D == 128 && G == 4) return launch_dg<128, 4, 2>(a, st);
     if (D == 128 && G == 8) return launch_dg<128, 8, 2>(a, st);
+    if (D == 128 && G == 12) return launch_dg<128, 12, 2>(a, st);
+    if (D == 128 && G == 16) return launch_dg<128, 16, 2>(a, st);
     if (D == 512 && G == 4) return launch_dg<512, 4, 1>(a, st);
     if (D == 512 && G == 8) return launch_dg<512, 8, 1>(a, st);
+    if (D == 512 && G == 12) return launch_dg<512, 12, 1>(a, st);
+    if (D == 512 && G == 16) return launch_dg<512, 16, 1>(a, st);
     return hipErrorInvalidValue;
 }
 

@@ -190,7 +190,10 @@ __global__ __launch_bounds__(64 * valu_waves<NQ>()) __attribute__((amdgpu_waves_
     const int c0 = base + split * piece;
     if (c0 >= L) return;
     const int kbeg = max(c0, lo);
-    const int kend = min(c0 + piece, L);
+    // a piece never runs past the host's longest piece (a.chunk, from max_seq_len): a device
+    // length above max_seq_len is a caller error, and this bound keeps its loads inside the
+    // chunk's cached table entries (and so inside the pool) rather than past them
+    const int kend = min(min(c0 + piece, c0 + a.chunk), L);
 
     // All query vectors of this KV head into LDS: vector v is row v / G, query head kvh*G + v%G.
     // Wave w computes vectors [VW*w, VW*w + VW).
@@ -437,6 +440,7 @@ bool valu_supported(int D, int G, int NQ) {
     if (D != 128 && D != 512) return false;
     if (G == 4) return NQ == 4 || NQ == 8 || NQ == 12;
     if (G == 8) return NQ == 8;
+    if (G == 12) return NQ == 12;
     return false;
 }
 
@@ -457,7 +461,9 @@ hipError_t launch_part_valu(int D, int G, int NQ, const PartArgs &a, int S, hipS
 #define KVP_VALU_CASE(d, g, nq) \
     if (D == d && G == g && NQ == nq) return launch_one<d, g, nq>(a, S, st);
     KVP_VALU_CASE(128, 4, 4) KVP_VALU_CASE(128, 4, 8) KVP_VALU_CASE(128, 4, 12) KVP_VALU_CASE(128, 8, 8)
+    KVP_VALU_CASE(128, 12, 12)
     KVP_VALU_CASE(512, 4, 4) KVP_VALU_CASE(512, 4, 8) KVP_VALU_CASE(512, 4, 12) KVP_VALU_CASE(512, 8, 8)
+    KVP_VALU_CASE(512, 12, 12)
 #undef KVP_VALU_CASE
     return hipErrorInvalidValue;
 }
