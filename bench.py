@@ -630,6 +630,9 @@ def main():
         log("[bench] side workloads only")
         res = {"side_only": True, "graphs": USE_GRAPHS,
                "other_workloads": other_workloads(torch, binding, staging, workloads, flush, cases)}
+        if args.calib_copy:
+            log("[bench] calibration copy")
+            calibration_copy(torch)
         print(json.dumps(res), flush=True)
         return
 

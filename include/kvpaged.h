@@ -121,8 +121,8 @@ kv_status kv_page_lease(kv_pool *pool, int32_t stream, int32_t n, int32_t *page_
 /* Lease policies.
  * KV_LEASE_QUEUE (the default): the first n ids of the free queue, in queue order.
  * KV_LEASE_CONTIGUOUS: keep each stream in runs of adjacent page ids while the pool has room,
- *   and fall back to scattered pages when it does not (TensorFold PR #1620, first review: the
- *   full layers may keep a contiguous cache until the pool needs the room).  The ids come from
+ *   and fall back to scattered pages when it does not (TensorFold PR #1620, first review, which
+ *   suggests one unbroken run of pages per full layer while the pool has space to spare).  The ids come from
  *   the first of these steps that applies:
  *   1. the stream holds pages, its last leased id is t, and t+1 .. t+n are all free: those;
  *   2. the longest run of adjacent free ids that holds n (the lowest such run on a tie), say
@@ -204,9 +204,11 @@ kv_status paged_attn_workspace_size(const kv_pool *pool, const kv_layout *lay,
 kv_status paged_attn_decode(const kv_pool *pool, const kv_layout *lay, const kv_attn_args *a,
                             void *hip_stream);
 
-/* kv_rows_put of one new row per stream followed by paged_attn_decode, in one launch
- * (TensorFold PR #1620, opening description, Writes and Reads bullets: a layer's new K/V row
- * is copied into the pages, then attention reads through the table).  k_new, v_new: device
+/* kv_rows_put of one new row per stream followed by paged_attn_decode (TensorFold PR #1620,
+ * opening description, Writes and Reads bullets: a layer's new K/V row is copied into the
+ * pages, then attention reads through the table), in one launch where the group has fewer than
+ * 16 query heads (the VALU kernel writes the row itself), else as a row-write launch followed
+ * by the attention on the same stream.  k_new, v_new: device
  * bf16 [S][1][Hkv][D] (16-byte aligned), written at position seq_len[s] - 1 exactly as
  * kv_rows_put writes it; the output and every byte of the pool afterwards equal those of the
  * two calls.  Errors as for decode, with KV_E_ARG for a null or misaligned k_new or v_new. */

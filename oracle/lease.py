@@ -16,8 +16,8 @@ so this library fixes one and the model states it:
     (The Kept states bullet resumes a kept state and reuses its pages; sharing the full pages of
     a common prefix is the form of that which copies nothing.)
 
-A second lease policy, "contiguous", follows the first review of the same PR (the full layers
-could keep a contiguous cache until the pool needs the room).  It hands out ids by the first
+A second lease policy, "contiguous", follows the first review of the same PR (its suggestion:
+the full layers stay in one unbroken run of pages for as long as the pool has space to spare).  It hands out ids by the first
 of these that applies, and removes them from the queue wherever they sit:
 
   1. extension: the stream holds pages, its newest is t, and t+1, ..., t+n are all free;

@@ -10,6 +10,7 @@ torch is imported before the library is loaded so that both use the one HIP runt
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 from ctypes import POINTER, c_float, c_int32, c_size_t, c_void_p
@@ -250,13 +251,16 @@ def _attend(entry: str, pool: Pool, q: torch.Tensor, table: torch.Tensor, seq_le
         raise ValueError("q must be [S][R][Hq][D]")
     _need(q, torch.bfloat16, "q")
     S, R, Hq, D = (int(x) for x in q.shape)
-    if out is None:
-        out = torch.empty_like(q)
-    _need(out, torch.bfloat16, "out", q.shape)
     lay = _layout(pool, table, seq_len, R, max_seq_len, ring_pages)
-    if workspace is None:
-        nbytes = workspace_size(pool, table, seq_len, R, Hq, max_seq_len, window, ring_pages)
-        workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=q.device)
+    # buffers this call allocates belong to the stream the kernels run on, so that the caching
+    # allocator does not hand their memory to other work before those kernels are done with it
+    with torch.cuda.stream(stream) if stream is not None else contextlib.nullcontext():
+        if out is None:
+            out = torch.empty_like(q)
+        if workspace is None:
+            nbytes = workspace_size(pool, table, seq_len, R, Hq, max_seq_len, window, ring_pages)
+            workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=q.device)
+    _need(out, torch.bfloat16, "out", q.shape)
     args = AttnArgs(_ptr(q), _ptr(out), Hq, float(scale), int(window), _ptr(workspace),
                     int(workspace.numel() * workspace.element_size()))
     _check(getattr(load(), entry)(pool.handle, ctypes.byref(lay), ctypes.byref(args), *extra,

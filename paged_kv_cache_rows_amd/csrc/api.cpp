@@ -177,6 +177,25 @@ kv_status make_plan(const kv_pool *pool, const kv_layout *lay, const kv_attn_arg
     return ok();
 }
 
+kvp::RowsArgs rows_args(const kv_pool *pool, const kv_layout *lay, const void *k_new, const void *v_new) {
+    kvp::RowsArgs ra;
+    ra.k_pages = pool->k_pages;
+    ra.v_pages = pool->v_pages;
+    ra.k_new = static_cast<const uint16_t *>(k_new);
+    ra.v_new = static_cast<const uint16_t *>(v_new);
+    ra.table = lay->page_table;
+    ra.seq_len = lay->seq_len;
+    ra.num_pages = pool->num_pages;
+    ra.P = pool->page_size;
+    ra.Hkv = pool->num_kv_heads;
+    ra.D = pool->head_dim;
+    ra.S = lay->num_streams;
+    ra.R = lay->rows;
+    ra.stride = lay->table_stride;
+    ra.ring_pages = lay->ring_pages;
+    return ra;
+}
+
 size_t workspace_bytes(const Plan &p) {
     return (size_t)p.S * p.R * p.Hq * p.n_splits * (p.D + 2) * sizeof(float);
 }
@@ -222,11 +241,17 @@ kv_status run_attention(const kv_pool *pool, const kv_layout *lay, const kv_attn
     pa.tree = tree;
     pa.k_new = static_cast<const uint16_t *>(k_new);
     pa.v_new = static_cast<const uint16_t *>(v_new);
-    if (k_new && p.mfma) return fail(KV_E_SHAPE, "%s: the fused row write has no MFMA kernel", who);
     pa.direct = (p.mfma && p.mp.direct) ? 1 : 0;
     const float scale = a->scale > 0.f ? a->scale : 1.0f / std::sqrt((float)p.D);
     pa.scale_log2 = scale * 1.4426950408889634f;
 
+    if (k_new && p.mfma) {
+        // the MFMA kernel has no fused row write: the row goes in first with the row-write
+        // kernel, on the same stream, so the attention reads it as kv_rows_put would leave it
+        pa.k_new = pa.v_new = nullptr;
+        const hipError_t e = kvp::launch_rows_put(rows_args(pool, lay, k_new, v_new), hs);
+        if (e != hipSuccess) return fail(KV_E_DEVICE, "%s: row-write launch failed: %s", who, hipGetErrorString(e));
+    }
     if (g_part_start && hipEventRecord(g_part_start, hs) != hipSuccess)
         return fail(KV_E_DEVICE, "%s: recording the start event failed", who);
     hipError_t e = p.mfma ? kvp::launch_part_mfma(p.D, p.G, p.mp, pa, p.S, hs)
@@ -492,22 +517,7 @@ kv_status kv_rows_put(const kv_pool *pool, const kv_layout *lay, const void *k_n
                     lay->ring_pages, pool->page_size);
     st = deep_check(pool, lay, lay->rows, hs, "kv_rows_put");
     if (st != KV_OK) return st;
-    kvp::RowsArgs ra;
-    ra.k_pages = pool->k_pages;
-    ra.v_pages = pool->v_pages;
-    ra.k_new = static_cast<const uint16_t *>(k_new);
-    ra.v_new = static_cast<const uint16_t *>(v_new);
-    ra.table = lay->page_table;
-    ra.seq_len = lay->seq_len;
-    ra.num_pages = pool->num_pages;
-    ra.P = pool->page_size;
-    ra.Hkv = pool->num_kv_heads;
-    ra.D = pool->head_dim;
-    ra.S = lay->num_streams;
-    ra.R = lay->rows;
-    ra.stride = lay->table_stride;
-    ra.ring_pages = lay->ring_pages;
-    const hipError_t e = kvp::launch_rows_put(ra, hs);
+    const hipError_t e = kvp::launch_rows_put(rows_args(pool, lay, k_new, v_new), hs);
     if (e != hipSuccess) return fail(KV_E_DEVICE, "kv_rows_put: launch failed: %s", hipGetErrorString(e));
     return ok();
 }

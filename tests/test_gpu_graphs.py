@@ -149,3 +149,28 @@ def test_calls_on_two_streams_at_once_match_the_default_stream():
     torch.cuda.synchronize()
     assert torch.equal(oa.view(torch.int16), ref_a.view(torch.int16))
     assert torch.equal(ob.view(torch.int16), ref_b.view(torch.int16))
+
+
+def test_calls_given_a_stream_allocate_their_buffers_on_it():
+    # no out and no workspace passed: the binding allocates both for the call, on the stream the
+    # kernels run on; meanwhile the default stream allocates, fills and frees buffers of the
+    # same sizes, which must never land in memory a side-stream call is still using
+    w = workloads.Workload(name="sa", streams=2, kv_heads=2, group=8, head_dim=128, page_size=64,
+                           rows=8, lengths=[3000, 1700], spare_frac=0.2, min_spares=2, seed=55)
+    c, _, _ = new_cache(w)
+    q = workloads.queries(w).cuda()
+    ref = binding.verify(c.pool, q, c.table, c.seq_len, c.max_seq_len)
+    torch.cuda.synchronize()
+    nbytes = binding.workspace_size(c.pool, c.table, c.seq_len, w.rows, w.q_heads, c.max_seq_len)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    outs = []
+    for _ in range(20):
+        outs.append(binding.verify(c.pool, q, c.table, c.seq_len, c.max_seq_len, stream=side))
+        junk = torch.full((nbytes,), 0xFF, dtype=torch.uint8, device="cuda")
+        junk2 = torch.full_like(q.view(torch.int16), 0x7FC0)
+        del junk, junk2
+    torch.cuda.synchronize()
+    for o in outs:
+        assert torch.equal(o.view(torch.int16), ref.view(torch.int16))
+    assert_close(ref, oracle_for(c, q), "verify on a side stream")

@@ -64,3 +64,34 @@ def test_groups_12_and_16_with_a_sliding_window(G, D, Hkv, R):
     c, _, _ = new_cache(w)
     q = workloads.queries(w).cuda()
     assert_close(attend(_entry(R), c, q, window=300), oracle_for(c, q, window=300), f"G={G} window 300")
+
+
+@pytest.mark.parametrize("G,D,Hkv,P", [(16, 512, 1, 512), (16, 128, 2, 37), (12, 128, 4, 64)])
+def test_decode_put_at_groups_12_and_16_equals_the_two_calls(G, D, Hkv, P):
+    # group 16 decodes on the MFMA kernel, where the row goes in through a row-write launch;
+    # group 12 on the VALU kernel, which writes the row itself: both equal kv_rows_put + decode
+    from paged_kv_cache_rows_amd import staging
+    from gpu_support import oracle_from_history, pool_bits
+    w = _w(Hkv, G, D, P, [3000, 700, 1], 1, seed=134)
+    say(f"decode_put G={G} D={D} P={P}")
+    order = workloads.free_order(w.pool_pages, 1341)
+    ks, vs = workloads.kv_history(w)
+    caches = []
+    for _ in range(2):
+        c = staging.make_cache(w, order=order)
+        staging.write_history(c, ks, vs, upto=[L - 1 for L in w.lengths])
+        caches.append(c)
+    a, b = caches
+    kn = torch.stack([ks[s][L - 1:L] for s, L in enumerate(w.lengths)]).cuda().contiguous()
+    vn = torch.stack([vs[s][L - 1:L] for s, L in enumerate(w.lengths)]).cuda().contiguous()
+    q = workloads.queries(w).cuda()
+    ml = max(w.lengths)
+    binding.rows_put(a.pool, a.table, a.seq_len, kn, vn, ml)
+    out_a = binding.decode(a.pool, q, a.table, a.seq_len, ml)
+    out_b = binding.decode_put(b.pool, q, b.table, b.seq_len, ml, kn, vn)
+    torch.cuda.synchronize()
+    assert torch.equal(out_a.view(torch.int16), out_b.view(torch.int16))
+    ka, va = pool_bits(a)
+    kb, vb = pool_bits(b)
+    assert (ka == kb).all() and (va == vb).all()
+    assert_close(out_b, oracle_from_history(ks, vs, q, w.lengths), f"decode_put G={G} D={D}")

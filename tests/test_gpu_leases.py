@@ -1,5 +1,5 @@
-"""GPU tests of the contiguous lease policy (TensorFold PR #1620, first review: the full
-layers could keep a contiguous cache until the pool needs the room).
+"""GPU tests of the contiguous lease policy (TensorFold PR #1620, first review, which suggests
+keeping the full layers in one unbroken run of pages while the pool has space to spare).
 
 Streams that grow side by side, a page at a time, lease under KV_LEASE_CONTIGUOUS from a pool
 that ends up nearly full, so most tables are one run of adjacent ids and some spill into a

@@ -611,8 +611,8 @@ def test_copy_pages_reads_sources_before_any_write():
 # ----------------------------------------------------------------------------- contiguous leases
 def _run_lease_golden(model_cls=None):
     """Drive a lease model through the hand-worked sequence of tests/golden/contiguous_leases.json
-    (TensorFold PR #1620, first review: keep the full layers contiguous until the pool needs
-    the room); AssertionError on the first difference."""
+    (TensorFold PR #1620, first review: the full layers in one unbroken run of pages while the
+    pool has space to spare); AssertionError on the first difference."""
     fx = json.load(open(os.path.join(os.path.dirname(GOLDEN), "contiguous_leases.json")))
     m = (model_cls or oracle.LeaseModel)(fx["num_pages"], fx["max_streams"])
     for st in fx["steps"]:
