@@ -18,7 +18,8 @@ from ctypes import POINTER, c_float, c_int32, c_size_t, c_void_p
 import numpy as np
 import torch
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkvpaged.so")
+# KVPAGED_LIB names another build of the library (the host sanitizer tests load one)
+LIB_PATH = os.environ.get("KVPAGED_LIB") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkvpaged.so")
 
 KV_OK, KV_E_ARG, KV_E_SHAPE, KV_E_NO_PAGES, KV_E_WORKSPACE, KV_E_DEVICE = 0, -1, -2, -3, -4, -5
 KV_LEASE_QUEUE, KV_LEASE_CONTIGUOUS = 0, 1

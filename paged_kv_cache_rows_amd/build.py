@@ -87,5 +87,58 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+RESOURCE_FIELDS = {"TotalSGPRs": "sgprs", "VGPRs": "vgprs", "AGPRs": "agprs", "ScratchSize [bytes/lane]": "scratch_bytes",
+                   "Occupancy [waves/SIMD]": "waves_per_simd", "SGPRs Spill": "sgpr_spill",
+                   "VGPRs Spill": "vgpr_spill", "LDS Size [bytes/block]": "lds_bytes"}
+RECORD_JSON = os.path.join(ROOT, "profiles", "kernel_resources.json")
+RECORD_MD = os.path.join(ROOT, "profiles", "kernel_resources.md")
+
+
+def parse_resources(path: str = os.path.join(BUILD, "resource_usage.txt")) -> dict:
+    """Per-kernel resource records from the compiler's kernel-resource-usage remarks of the last
+    build: {demangled name: {sgprs, vgprs, agprs, scratch_bytes, waves_per_simd, sgpr_spill,
+    vgpr_spill, lds_bytes}}."""
+    recs, cur = {}, None
+    with open(path) as f:
+        for ln in f:
+            if "remark:" not in ln:
+                continue
+            body = ln.split("remark:", 1)[1].split("[-Rpass", 1)[0].strip()
+            key, _, val = body.partition(":")
+            key, val = key.strip(), val.strip()
+            if key == "Function Name":
+                cur = val
+                recs[cur] = {}
+            elif cur is not None and key in RESOURCE_FIELDS:
+                recs[cur][RESOURCE_FIELDS[key]] = int(val)
+    names = list(recs)
+    p = subprocess.run(["c++filt"], input="\n".join(names), capture_output=True, text=True)
+    demangled = p.stdout.splitlines() if p.returncode == 0 and len(p.stdout.splitlines()) == len(names) else names
+    return {d: recs[n] for n, d in zip(names, demangled)}
+
+
+def write_record():
+    """Write the current build's per-kernel resources to profiles/ (JSON and a Markdown table)."""
+    import json
+    recs = parse_resources()
+    with open(RECORD_JSON, "w") as f:
+        json.dump(recs, f, indent=1, sort_keys=True)
+        f.write("\n")
+    cols = ["vgprs", "agprs", "sgprs", "scratch_bytes", "vgpr_spill", "sgpr_spill", "lds_bytes", "waves_per_simd"]
+    lines = ["# Kernel resources (gfx950, hipcc of ROCm 7.2, -O3)", "",
+             "Written by `python -m paged_kv_cache_rows_amd.build --record` from the compiler's",
+             "kernel-resource-usage remarks of the build (`_build/resource_usage.txt`); "
+             "`tests/test_kernel_resources.py` fails",
+             "when a kernel spills or when the build no longer matches this record.", "",
+             "| kernel | " + " | ".join(cols) + " |", "|---|" + "---:|" * len(cols)]
+    for name in sorted(recs):
+        r = recs[name]
+        lines.append(f"| `{name}` | " + " | ".join(str(r.get(c, "")) for c in cols) + " |")
+    with open(RECORD_MD, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
 if __name__ == "__main__":
     print(build(verbose="--verbose" in sys.argv))
+    if "--record" in sys.argv:
+        write_record()

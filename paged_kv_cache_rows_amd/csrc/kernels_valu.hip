@@ -155,8 +155,11 @@ int valu_mode(int P, int chunk) {
     return 2;
 }
 
+// At d 128 with 8 query vectors the kernel keeps four waves per SIMD (128 registers); the
+// per-row lookups of MODE 2 (tiny pages) need a few more registers than that and would spill,
+// so that mode has no occupancy floor.
 template <int D, int G, int NQ, int MODE>
-__global__ __launch_bounds__(64 * valu_waves<NQ>()) __attribute__((amdgpu_waves_per_eu(D == 128 && NQ == 8 ? 4 : 1, 8))) void part_valu_kernel(const PartArgs a) {
+__global__ __launch_bounds__(64 * valu_waves<NQ>()) __attribute__((amdgpu_waves_per_eu(D == 128 && NQ == 8 && MODE != 2 ? 4 : 1, 8))) void part_valu_kernel(const PartArgs a) {
     using Geo = ValuGeom<D>;
     constexpr int LPR = Geo::LPR, RPI = Geo::RPI, NB = Geo::NB, QL = Geo::QL, SEG = Geo::SEG;
     constexpr int RS = Geo::RS, TC = Geo::TC;
