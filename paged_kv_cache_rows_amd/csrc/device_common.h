@@ -76,6 +76,15 @@ __device__ __forceinline__ float wave_sum(float x) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// A wave-uniform int32 read from global memory with a vector load, so that it is issued
+// together with the other loads at the start of a kernel and one wait covers them all (a
+// scalar load is scheduled on its own, after the vector loads have been waited for).  The
+// lane-dependent zero from mbcnt makes the address look per-lane to the compiler.
+__device__ __forceinline__ int load_uniform_i32(const int32_t *p) {
+    const int z = __builtin_amdgcn_mbcnt_lo(0u, 0u);
+    return *(p + z);
+}
+
 // A 16-byte load of K/V page data with the nontemporal hint, for the decode kernel, which reads
 // every K/V byte of a call once: streaming it through the caches rather than keeping it there
 // raises the achieved HBM rate of the 12-stream decode from about 5.6 to 5.9-6.3 TB/s.  (The

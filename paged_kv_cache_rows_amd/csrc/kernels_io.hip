@@ -108,9 +108,28 @@ __global__ __launch_bounds__(64) void merge_kernel(const MergeArgs a) {
     const int cw = blockIdx.x % NCW;        // channel slice
     const int s = vec / (a.R * a.Hq);
     const int r = (vec / a.Hq) % a.R;
-    const int L = a.seq_len[s];
     const int lane = threadIdx.x;
     const int cb = lane % CB, sg = lane / CB;
+    const float2 *ml = reinterpret_cast<const float2 *>(a.ws_ml) + (size_t)vec * a.n_splits;
+    const float *acc = a.ws_acc + (size_t)vec * a.n_splits * D + cw * CW + cb * 8;
+    // Without a window every row's splits start at split 0, so when they fit one pass the
+    // partials are loaded before the stream's length is known (slots the row turns out not to
+    // read are discarded by select below): the merge then costs one round trip to memory.
+    const bool early = a.window <= 0 && a.n_splits <= 4 * SG;
+    float4 xe[4][2];
+    float2 mle[4];
+    if (early) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int i = u * SG + sg;
+            const int ic = i < a.n_splits ? i : 0;
+            mle[u] = ml[ic];
+            const float4 *src = reinterpret_cast<const float4 *>(acc + (size_t)ic * D);
+            xe[u][0] = src[0];
+            xe[u][1] = src[1];
+        }
+    }
+    const int L = a.seq_len[s];
     const int pos = L - a.R + r;
     float num[8];
 #pragma unroll
@@ -132,24 +151,34 @@ __global__ __launch_bounds__(64) void merge_kernel(const MergeArgs a) {
             i_begin = lo_r / a.chunk - first;
             n = min(pos / a.chunk - first + 1, a.n_splits);
         }
-        const float2 *ml = reinterpret_cast<const float2 *>(a.ws_ml) + (size_t)vec * a.n_splits;
-        const float *acc = a.ws_acc + (size_t)vec * a.n_splits * D + cw * CW + cb * 8;
         if (n - i_begin <= 4 * SG) {
             // one pass (every decode and verify plan here): the partials and their (m, l) are
-            // loaded together, before the max is known, so the row costs one round trip to
-            // memory after the length, not two
+            // loaded together, before the max is known
             float4 x[4][2];
             float2 m_l[4];
+            if (early) {
+                // i_begin is 0 here; a slot past the row's splits may never have been written
+                // (possibly NaN): it becomes an empty split, so that a zero weight never meets it
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int i = i_begin + u * SG + sg;
-                // a padded slot rereads the row's first split, which is always written (a zero
-                // weight must never meet an unwritten, possibly NaN, split)
-                const int ic = i < n ? i : i_begin;
-                m_l[u] = ml[ic];
-                const float4 *src = reinterpret_cast<const float4 *>(acc + (size_t)ic * D);
-                x[u][0] = src[0];
-                x[u][1] = src[1];
+                for (int u = 0; u < 4; ++u) {
+                    const bool in = u * SG + sg < n;
+                    m_l[u] = in ? mle[u] : make_float2(-INFINITY, 0.f);
+                    const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
+                    x[u][0] = in ? xe[u][0] : z;
+                    x[u][1] = in ? xe[u][1] : z;
+                }
+            } else {
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int i = i_begin + u * SG + sg;
+                    // a padded slot rereads the row's first split, which is always written (a
+                    // zero weight must never meet an unwritten, possibly NaN, split)
+                    const int ic = i < n ? i : i_begin;
+                    m_l[u] = ml[ic];
+                    const float4 *src = reinterpret_cast<const float4 *>(acc + (size_t)ic * D);
+                    x[u][0] = src[0];
+                    x[u][1] = src[1];
+                }
             }
 #pragma unroll
             for (int u = 0; u < 4; ++u) M = fmaxf(M, m_l[u].x);

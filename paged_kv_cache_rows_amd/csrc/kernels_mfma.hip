@@ -210,10 +210,55 @@ __global__ __launch_bounds__(256 * KS) void part_mfma_kernel(const PartArgs a) {
     const int kvh = (item / (a.tiles * a.n_splits)) % a.Hkv;
     const int s = item / (a.tiles * a.n_splits * a.Hkv);
     const int R = a.R, W = a.window, CH = a.chunk;
-    const int L = a.seq_len[s];
     const int NQ = R * G;
     const int v0 = tile * M;
     if (v0 >= NQ || split >= a.n_splits) return;
+    const int32_t *trow = a.table + (size_t)s * a.stride;
+
+    // This lane's query columns and the queries as the B operand of S^T = K Q^T (the lane holds
+    // channels 32 kb + 8 grp .. + 8 of its column), a tree window's ancestor bits, and, when the
+    // stream's whole page table fits the cache (a full layer of at most TC pages), its table
+    // entries: none of them depends on the stream's length, so they are loaded together with
+    // it, and the first K/V loads wait for one round trip to memory rather than two.
+    const bool whole = MODE != 2 && a.ring_pages == 0 && a.stride <= TC;
+    const int Lv = load_uniform_i32(a.seq_len + s);
+    bool col_ok[QW];
+    int rq[QW], hq[QW];
+    uint32_t anc[QW];                                 // ancestor bits of the column's row
+    bf16x8_t qf[QW][NKB];
+#pragma unroll
+    for (int b = 0; b < QW; ++b) {
+        const int vq = v0 + (wave * QW + b) * 16 + col;
+        col_ok[b] = vq < NQ;
+        rq[b] = col_ok[b] ? vq / G : 0;
+        hq[b] = kvh * G + (col_ok[b] ? vq % G : 0);
+        anc[b] = a.tree ? a.tree[s * R + rq[b]] : 0xFFFFFFFFu;
+        const uint16_t *qrow = a.q + ((size_t)(s * R + rq[b]) * a.Hq + hq[b]) * D + 8 * grp;
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+            u32x4 x = *reinterpret_cast<const u32x4 *>(qrow + 32 * kb);
+            if (!col_ok[b]) x = u32x4{0, 0, 0, 0};
+            qf[b][kb] = __builtin_bit_cast(bf16x8_t, x);
+        }
+    }
+    constexpr int TPT = (TC + NTH - 1) / NTH;         // table entries per thread
+    int tv[TPT];
+    if (whole) {
+#pragma unroll
+        for (int k = 0; k < TPT; ++k) {
+            const int i = tid + k * NTH;
+            tv[k] = i < a.stride ? trow[i] : -1;
+        }
+    }
+    const int L = __builtin_amdgcn_readfirstlane(Lv);
+    if (whole) {
+#pragma unroll
+        for (int k = 0; k < TPT; ++k) {
+            const int i = tid + k * NTH;
+            if (i < TC) t_lds[i] = ((unsigned)tv[k] < (unsigned)a.num_pages) ? tv[k] : -1;
+        }
+    }
+
     const int r_first = v0 / G;
     const int r_last = (min(NQ, v0 + M) - 1) / G;
     const int p_first = L - R + r_first, p_last = L - R + r_last;
@@ -245,29 +290,11 @@ __global__ __launch_bounds__(256 * KS) void part_mfma_kernel(const PartArgs a) {
     // ... and <= this (with a tree-shaped window, only the keys before the window)
     const int hi_full = a.tree ? min(p_first, L - R - 1) : p_first;
     const int win0 = L - R;                           // first slot of the window
-
-    // this lane's query columns, and the queries as the B operand of S^T = K Q^T: the lane
-    // holds channels 32 kb + 8 grp .. + 8 of its column
-    bool col_ok[QW];
-    int rq[QW], hq[QW], p_col[QW], lo_col[QW];
-    uint32_t anc[QW];                                 // ancestor bits of the column's row
-    bf16x8_t qf[QW][NKB];
+    int p_col[QW], lo_col[QW];
 #pragma unroll
     for (int b = 0; b < QW; ++b) {
-        const int vq = v0 + (wave * QW + b) * 16 + col;
-        col_ok[b] = vq < NQ;
-        rq[b] = col_ok[b] ? vq / G : 0;
-        hq[b] = kvh * G + (col_ok[b] ? vq % G : 0);
         p_col[b] = L - R + rq[b];
         lo_col[b] = W > 0 ? p_col[b] - W + 1 : 0;
-        anc[b] = a.tree ? a.tree[s * R + rq[b]] : 0xFFFFFFFFu;
-        const uint16_t *qrow = a.q + ((size_t)(s * R + rq[b]) * a.Hq + hq[b]) * D + 8 * grp;
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) {
-            u32x4 x = *reinterpret_cast<const u32x4 *>(qrow + 32 * kb);
-            if (!col_ok[b]) x = u32x4{0, 0, 0, 0};
-            qf[b][kb] = __builtin_bit_cast(bf16x8_t, x);
-        }
     }
 
     // a wave whose query columns all lie past the tile's vectors (a partly filled tile: 4 rows
@@ -278,9 +305,9 @@ __global__ __launch_bounds__(256 * KS) void part_mfma_kernel(const PartArgs a) {
     const int P = a.P;
     const int kt_first = (kbeg / KT) * KT;
     const int nt = (kend - kt_first + KT - 1) / KT;     // KT-key sub-tiles
-    const int idx0 = kt_first / P;
-    const int32_t *trow = a.table + (size_t)s * a.stride;
-    if (MODE != 2) {
+    // otherwise the entries from the logical page of the split's first tile on
+    const int idx0 = whole ? 0 : kt_first / P;
+    if (MODE != 2 && !whole) {
         for (int i = tid; i < TC; i += NTH) {
             int idx = idx0 + i;
             if (a.ring_pages) idx %= a.ring_pages;

@@ -155,11 +155,12 @@ int valu_mode(int P, int chunk) {
     return 2;
 }
 
-// At d 128 with 8 query vectors the kernel keeps four waves per SIMD (128 registers); the
-// per-row lookups of MODE 2 (tiny pages) need a few more registers than that and would spill,
-// so that mode has no occupancy floor.
+// At d 128 with 8 query vectors and one lookup per batch (MODE 0, pages a multiple of the
+// batch: the headline) the kernel keeps four waves per SIMD (128 registers); the per-row
+// lookups of MODEs 1 and 2 need a few more registers than that and would spill, so those modes
+// have no occupancy floor.
 template <int D, int G, int NQ, int MODE>
-__global__ __launch_bounds__(64 * valu_waves<NQ>()) __attribute__((amdgpu_waves_per_eu(D == 128 && NQ == 8 && MODE != 2 ? 4 : 1, 8))) void part_valu_kernel(const PartArgs a) {
+__global__ __launch_bounds__(64 * valu_waves<NQ>()) __attribute__((amdgpu_waves_per_eu(D == 128 && NQ == 8 && MODE == 0 ? 4 : 1, 8))) void part_valu_kernel(const PartArgs a) {
     using Geo = ValuGeom<D>;
     constexpr int LPR = Geo::LPR, RPI = Geo::RPI, NB = Geo::NB, QL = Geo::QL, SEG = Geo::SEG;
     constexpr int RS = Geo::RS, TC = Geo::TC;
@@ -184,7 +185,54 @@ __global__ __launch_bounds__(64 * valu_waves<NQ>()) __attribute__((amdgpu_waves_
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int split = blockIdx.x, kvh = blockIdx.y, s = blockIdx.z;
-    const int L = a.seq_len[s];
+    const int32_t *trow = a.table + (size_t)s * a.stride;
+
+    // All query vectors of this KV head go to LDS (vector v is row v / G, query head
+    // kvh*G + v%G; wave w computes vectors [VW*w, VW*w + VW)), and so do the page-table entries
+    // the workgroup reads (logical page idx0 + i at entry i; entries past the table or outside
+    // the pool become -1).  When the stream's whole table fits the cache (a full layer of at
+    // most TC pages), idx0 is 0 and the entries, like the queries, do not depend on the
+    // stream's length: both are loaded before the length, so that the first K/V loads wait for
+    // one round trip to memory, not two.
+    constexpr int QN = NQ * (D / 8);                          // 16-byte query pieces
+    constexpr int QPT = (QN + 64 * NW - 1) / (64 * NW);       // per thread
+    constexpr int TPT = (TC + 64 * NW - 1) / (64 * NW);       // table entries per thread
+    const bool whole = MODE != 2 && a.ring_pages == 0 && a.stride <= TC;
+    const int Lv = load_uniform_i32(a.seq_len + s);
+    u32x4 qv[QPT];
+    int tv[TPT];
+#pragma unroll
+    for (int k = 0; k < QPT; ++k) {
+        const int i = tid + k * 64 * NW;
+        if (i < QN) {
+            const int v = i / (D / 8), c = i - (i / (D / 8)) * (D / 8);
+            qv[k] = *reinterpret_cast<const u32x4 *>(a.q + ((size_t)(s * R + v / G) * a.Hq + kvh * G + (v % G)) * D + c * 8);
+        }
+    }
+    if (whole) {
+#pragma unroll
+        for (int k = 0; k < TPT; ++k) {
+            const int i = tid + k * 64 * NW;
+            tv[k] = i < a.stride ? trow[i] : -1;
+        }
+    }
+    const int L = __builtin_amdgcn_readfirstlane(Lv);
+#pragma unroll
+    for (int k = 0; k < QPT; ++k) {
+        const int i = tid + k * 64 * NW;
+        if (i < QN) {
+            const int v = i / (D / 8), c = i - (i / (D / 8)) * (D / 8);
+            *reinterpret_cast<u32x4 *>(q_lds + v * RS + c * 8) = qv[k];
+        }
+    }
+    if (whole) {
+#pragma unroll
+        for (int k = 0; k < TPT; ++k) {
+            const int i = tid + k * 64 * NW;
+            if (i < TC) t_lds[i] = ((unsigned)tv[k] < (unsigned)a.num_pages) ? tv[k] : -1;
+        }
+    }
+
     const int W = a.window;
     const int lo = W > 0 ? max(0, L - R - W + 1) : 0;
     if (L <= 0 || split >= a.n_splits) return;
@@ -198,26 +246,16 @@ __global__ __launch_bounds__(64 * valu_waves<NQ>()) __attribute__((amdgpu_waves_
     // chunk's cached table entries (and so inside the pool) rather than past them
     const int kend = min(min(c0 + piece, c0 + a.chunk), L);
 
-    // All query vectors of this KV head into LDS: vector v is row v / G, query head kvh*G + v%G.
-    // Wave w computes vectors [VW*w, VW*w + VW).
-    for (int i = tid; i < NQ * (D / 8); i += 64 * NW) {
-        const int v = i / (D / 8), c = i - (i / (D / 8)) * (D / 8);
-        *reinterpret_cast<u32x4 *>(q_lds + v * RS + c * 8) =
-            *reinterpret_cast<const u32x4 *>(a.q + ((size_t)(s * R + v / G) * a.Hq + kvh * G + (v % G)) * D + c * 8);
-    }
-
     const int lrow = lane / LPR;            // row inside a group of RPI rows (load and PV)
     const int lch = lane - lrow * LPR;      // 16-byte piece of the row
     const size_t page_elems = (size_t)a.Hkv * a.P * D;
     const size_t head_off = (size_t)kvh * a.P * D + (size_t)lch * 8;
-    const int32_t *trow = a.table + (size_t)s * a.stride;
     const int P = a.P;
     const int b_first = (kbeg / NB) * NB;
 
-    // The chunk's page-table entries, looked up once per chunk into LDS (logical page index
-    // idx0 + i); entries past the table or outside the pool become -1.
-    const int idx0 = b_first / P;
-    if (MODE != 2) {
+    // otherwise the chunk's entries, from the logical page of its first batch on
+    const int idx0 = whole ? 0 : b_first / P;
+    if (MODE != 2 && !whole) {
         for (int i = tid; i < TC; i += 64 * NW) {
             int idx = idx0 + i;
             if (a.ring_pages) idx %= a.ring_pages;
@@ -240,7 +278,8 @@ __global__ __launch_bounds__(64 * valu_waves<NQ>()) __attribute__((amdgpu_waves_
             int idx = (L - 1) / P;
             const int off = (L - 1) - idx * P;
             if (a.ring_pages) idx %= a.ring_pages;
-            const int pg = idx < a.stride ? trow[idx] : -1;
+            // with the whole table cached, its entry is already in LDS (validated, -1 if bad)
+            const int pg = whole ? t_lds[idx] : (idx < a.stride ? trow[idx] : -1);
             if ((unsigned)pg < (unsigned)a.num_pages) {
                 const size_t dst = (size_t)pg * page_elems + head_off + (size_t)off * D;   // head_off has the lane's 8 channels
                 *reinterpret_cast<u32x4 *>(const_cast<uint16_t *>(a.k_pages) + dst) =
