@@ -107,7 +107,9 @@ typedef struct kv_attn_args {
  * 8, or a free_order that is not a permutation of [0, num_pages). */
 kv_status kv_pool_create(const kv_pool_desc *desc, kv_pool **out);
 
-/* Destroy the host metadata (never the caller's pages).  NULL is accepted. */
+/* Destroy the host metadata (never the caller's pages).  NULL is accepted.  (The pool is the
+ * arena of TensorFold PR #1620's opening description; its memory stays the caller's, as the
+ * buffers of the launcher on the metrale glm5next_dsa select.rs page are its caller's.) */
 kv_status kv_pool_destroy(kv_pool *pool);
 
 /* Lease n pages to a stream as it grows (TensorFold PR #1620, opening description: streams
@@ -186,7 +188,10 @@ kv_status kv_pages_copy(const kv_pool *pool, const int32_t *src_ids, const int32
 
 /* Bytes of workspace that a decode/verify/prefill call with these arguments needs: a function
  * of the call's shape only (S, R, Hkv, Hq, D, max_seq_len, window), never of the device
- * lengths or the table.  It holds the split partials (D + 2 floats per query vector and
+ * lengths or the table.  The convention is that of the metrale glm5next_dsa select.rs page
+ * (module invariants and the scratch `fits` check: scratch is sized from the launch geometry
+ * ahead of time, and a pass that needs more than was allocated is an error, not an overrun): every attention call checks its workspace
+ * against this size before any launch and returns KV_E_WORKSPACE when it is smaller.  It holds the split partials (D + 2 floats per query vector and
  * split).  A call whose query tiles fill the GPU by themselves uses one split and writes its
  * output directly; it still asks for, and is checked against, this size. */
 kv_status paged_attn_workspace_size(const kv_pool *pool, const kv_layout *lay,
@@ -262,7 +267,9 @@ kv_status paged_attn_prefill(const kv_pool *pool, const kv_layout *lay, const kv
  * hipEventElapsedTime.  NULL, NULL turns it off.  The events are the caller's. */
 kv_status kv_set_part_events(void *start_event, void *stop_event);
 
-/* Text of the calling thread's last non-OK status ("" if none). */
+/* Text of the calling thread's last non-OK status ("" if none): the reason a call was refused
+ * before any launch (as the plan and scratch checks on the metrale glm5next_dsa select.rs page
+ * fail with a message rather than launching). */
 const char *kv_last_error(void);
 
 /* KVPAGED_ABI_VERSION of the built library. */
