@@ -27,8 +27,9 @@
  *   - Table contents and device lengths are trusted on the hot path; with the environment
  *     variable KVP_CHECK=1 every call copies them to the host first (synchronously) and refuses
  *     bad ones with KV_E_ARG.  Without it, a page id outside [0, num_pages) is never
- *     dereferenced (its rows read as zeros and are not written), so a bad table gives a wrong
- *     result but touches no memory outside the pool.
+ *     dereferenced (attention reads page 0 in its place; row writes skip it) and a length
+ *     above max_seq_len is read as max_seq_len, so a bad table or length gives a wrong result
+ *     but touches no memory outside the pool, the table and the workspace.
  */
 #ifndef KVPAGED_H
 #define KVPAGED_H
@@ -82,7 +83,10 @@ typedef struct kv_layout {
                                   rows; the call's rows sit at positions L-R .. L-1, and rows at
                                   negative positions (R > L) are not written and see no key */
     int32_t max_seq_len;       /* host: an upper bound of seq_len over the call (sizes grids and
-                                  the workspace; a larger device length is a caller error) */
+                                  the workspace).  A larger device length is a caller error: the
+                                  kernels read it as max_seq_len, so every access stays inside
+                                  the table and workspace planned for the call, and KVP_CHECK=1
+                                  refuses it before launch */
     int32_t ring_pages;        /* 0: full layer, position j lives in page table[j / P];
                                   n > 0: ring of n pages, position j lives in
                                   table[(j / P) % n], so only the newest n*P positions exist */

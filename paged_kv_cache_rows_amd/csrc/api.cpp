@@ -112,21 +112,9 @@ kv_status deep_check(const kv_pool *pool, const kv_layout *lay, int64_t ring_spa
 }
 
 struct Plan {
-    bool mfma;
-    int D, G, Hkv, Hq, S, R, chunk, n_splits;
-    bool even;   // VALU: even pieces per stream; MFMA: absolute chunks of `chunk` keys
-    int align;
-    kvp::MfmaPlan mp;
+    int D, G, Hkv, Hq, S, R;
+    kvp::CallPlan cp;
 };
-
-int splits_for(int max_seq_len, int rows, int window, int chunk) {
-    int n = ceil_div(max_seq_len, chunk);
-    if (window > 0) {
-        const int span = ceil_div((int64_t)window + rows - 1, chunk) + 1;
-        if (span < n) n = span;
-    }
-    return n < 1 ? 1 : n;
-}
 
 kv_status make_plan(const kv_pool *pool, const kv_layout *lay, const kv_attn_args *a, Plan *p, const char *who) {
     kv_status st = check_layout(pool, lay, who);
@@ -148,32 +136,9 @@ kv_status make_plan(const kv_pool *pool, const kv_layout *lay, const kv_attn_arg
     p->G = p->Hq / p->Hkv;
     p->S = lay->num_streams;
     p->R = lay->rows;
-    const int nq = p->R * p->G;
-    p->mfma = nq >= 16;
-    if (p->mfma) {
-        if (!kvp::mfma_supported(p->D, p->G, p->R))
-            return fail(KV_E_SHAPE, "%s: no MFMA kernel for head_dim %d, group %d, rows %d", who, p->D, p->G, p->R);
-        p->mp = kvp::mfma_plan(p->D, p->G, p->R, p->S, p->Hkv, pool->page_size, lay->max_seq_len, a->window);
-        p->chunk = p->mp.chunk;
-    } else {
-        if (!kvp::valu_supported(p->D, p->G, nq))
-            return fail(KV_E_SHAPE, "%s: no VALU kernel for head_dim %d, group %d, rows %d", who, p->D, p->G, p->R);
-        // L - base is at most max_seq_len, or the window plus the rows plus the alignment
-        int span = lay->max_seq_len;
-        const int align = p->D == 512 ? 16 : 64;
-        if (a->window > 0 && (int64_t)a->window + p->R - 1 + align - 1 < span)
-            span = a->window + p->R - 1 + align - 1;
-        const kvp::ValuPlan vp = kvp::valu_plan(p->D, nq, p->S, p->Hkv, span < 1 ? 1 : span);
-        p->chunk = vp.max_piece;
-        p->n_splits = vp.n_splits;
-        p->even = true;
-        p->align = vp.align;
-    }
-    if (p->mfma) {
-        p->n_splits = p->mp.direct ? 1 : splits_for(lay->max_seq_len, p->R, a->window, p->chunk);
-        p->even = false;
-        p->align = 1;
-    }
+    if (!kvp::call_plan(p->D, p->G, p->R, p->S, p->Hkv, pool->page_size, lay->max_seq_len, a->window, &p->cp))
+        return fail(KV_E_SHAPE, "%s: no %s kernel for head_dim %d, group %d, rows %d", who,
+                    p->R * p->G >= 16 ? "MFMA" : "VALU", p->D, p->G, p->R);
     return ok();
 }
 
@@ -193,11 +158,12 @@ kvp::RowsArgs rows_args(const kv_pool *pool, const kv_layout *lay, const void *k
     ra.R = lay->rows;
     ra.stride = lay->table_stride;
     ra.ring_pages = lay->ring_pages;
+    ra.max_len = lay->max_seq_len;
     return ra;
 }
 
 size_t workspace_bytes(const Plan &p) {
-    return (size_t)p.S * p.R * p.Hq * p.n_splits * (p.D + 2) * sizeof(float);
+    return (size_t)p.S * p.R * p.Hq * p.cp.n_splits * (p.D + 2) * sizeof(float);
 }
 
 kv_status run_attention(const kv_pool *pool, const kv_layout *lay, const kv_attn_args *a, void *hip_stream,
@@ -226,26 +192,27 @@ kv_status run_attention(const kv_pool *pool, const kv_layout *lay, const kv_attn
     pa.seq_len = lay->seq_len;
     pa.q = static_cast<const uint16_t *>(a->q);
     pa.ws_acc = static_cast<float *>(a->workspace);
-    pa.ws_ml = pa.ws_acc + (size_t)p.S * p.R * p.Hq * p.n_splits * p.D;
+    pa.ws_ml = pa.ws_acc + (size_t)p.S * p.R * p.Hq * p.cp.n_splits * p.D;
     pa.num_pages = pool->num_pages;
     pa.P = pool->page_size;
     pa.Hkv = p.Hkv;
     pa.stride = lay->table_stride;
     pa.ring_pages = lay->ring_pages;
+    pa.max_len = lay->max_seq_len;
     pa.R = p.R;
     pa.Hq = p.Hq;
     pa.window = a->window;
-    pa.n_splits = p.n_splits;
-    pa.chunk = p.chunk;
+    pa.n_splits = p.cp.n_splits;
+    pa.chunk = p.cp.chunk;
     pa.out = static_cast<uint16_t *>(a->out);
     pa.tree = tree;
     pa.k_new = static_cast<const uint16_t *>(k_new);
     pa.v_new = static_cast<const uint16_t *>(v_new);
-    pa.direct = (p.mfma && p.mp.direct) ? 1 : 0;
+    pa.direct = (p.cp.mfma && p.cp.mp.direct) ? 1 : 0;
     const float scale = a->scale > 0.f ? a->scale : 1.0f / std::sqrt((float)p.D);
     pa.scale_log2 = scale * 1.4426950408889634f;
 
-    if (k_new && p.mfma) {
+    if (k_new && p.cp.mfma) {
         // the MFMA kernel has no fused row write: the row goes in first with the row-write
         // kernel, on the same stream, so the attention reads it as kv_rows_put would leave it
         pa.k_new = pa.v_new = nullptr;
@@ -254,7 +221,7 @@ kv_status run_attention(const kv_pool *pool, const kv_layout *lay, const kv_attn
     }
     if (g_part_start && hipEventRecord(g_part_start, hs) != hipSuccess)
         return fail(KV_E_DEVICE, "%s: recording the start event failed", who);
-    hipError_t e = p.mfma ? kvp::launch_part_mfma(p.D, p.G, p.mp, pa, p.S, hs)
+    hipError_t e = p.cp.mfma ? kvp::launch_part_mfma(p.D, p.G, p.cp.mp, pa, p.S, hs)
                           : kvp::launch_part_valu(p.D, p.G, p.R * p.G, pa, p.S, hs);
     if (e != hipSuccess) return fail(KV_E_DEVICE, "%s: part kernel launch failed: %s", who, hipGetErrorString(e));
     if (g_part_stop && hipEventRecord(g_part_stop, hs) != hipSuccess)
@@ -272,10 +239,11 @@ kv_status run_attention(const kv_pool *pool, const kv_layout *lay, const kv_attn
     ma.Hq = p.Hq;
     ma.D = p.D;
     ma.window = a->window;
-    ma.n_splits = p.n_splits;
-    ma.chunk = p.chunk;
-    ma.even = p.even ? 1 : 0;
-    ma.align = p.align;
+    ma.max_len = lay->max_seq_len;
+    ma.n_splits = p.cp.n_splits;
+    ma.chunk = p.cp.chunk;
+    ma.even = p.cp.even ? 1 : 0;
+    ma.align = p.cp.align;
     e = kvp::launch_merge(ma, hs);
     if (e != hipSuccess) return fail(KV_E_DEVICE, "%s: merge launch failed: %s", who, hipGetErrorString(e));
     return ok();
@@ -323,6 +291,47 @@ std::vector<int32_t> contiguous_pick(const kv_pool *pool, const std::vector<int3
 }
 
 }  // namespace
+
+namespace kvp {
+
+// Splits of an MFMA call that is not direct: the chunks from the first one any row of a stream
+// sees to the stream's end (max_seq_len bounds the end; a window bounds the count).
+static int splits_for(int max_seq_len, int rows, int window, int chunk) {
+    int n = (int)(((int64_t)max_seq_len + chunk - 1) / chunk);
+    if (window > 0) {
+        const int span = (int)(((int64_t)window + rows - 1 + chunk - 1) / chunk) + 1;
+        if (span < n) n = span;
+    }
+    return n < 1 ? 1 : n;
+}
+
+bool call_plan(int D, int G, int R, int S, int Hkv, int P, int max_seq_len, int window, CallPlan *p) {
+    const int nq = R * G;
+    p->mfma = nq >= 16;
+    if (p->mfma) {
+        if (!mfma_supported(D, G, R)) return false;
+        p->mp = mfma_plan(D, G, R, S, Hkv, P, max_seq_len, window);
+        p->chunk = p->mp.chunk;
+        p->n_splits = p->mp.direct ? 1 : splits_for(max_seq_len, R, window, p->chunk);
+        p->even = false;
+        p->align = 1;
+        return true;
+    }
+    if (!valu_supported(D, G, nq)) return false;
+    // L - base is at most max_seq_len, or the window plus the rows plus the alignment
+    int span = max_seq_len;
+    const int align = D == 512 ? 16 : 64;
+    if (window > 0 && (int64_t)window + R - 1 + align - 1 < span) span = window + R - 1 + align - 1;
+    const ValuPlan vp = valu_plan(D, nq, S, Hkv, span < 1 ? 1 : span);
+    p->mp = MfmaPlan{};
+    p->chunk = vp.max_piece;
+    p->n_splits = vp.n_splits;
+    p->even = true;
+    p->align = vp.align;
+    return true;
+}
+
+}  // namespace kvp
 
 extern "C" {
 

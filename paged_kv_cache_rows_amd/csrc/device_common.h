@@ -85,6 +85,15 @@ __device__ __forceinline__ int load_uniform_i32(const int32_t *p) {
     return *(p + z);
 }
 
+// Page id of entry i of a workgroup's cached page-table entries (TC of them, -1 for an absent
+// page).  An index outside the cache counts as absent: only rows past the keys a workgroup
+// uses produce one (the tail of its last load step), and those rows are masked out.  Absent
+// pages read page 0, which is always inside the pool.
+template <int TC>
+__device__ __forceinline__ int cached_page(const int32_t *t, int i) {
+    return (unsigned)i < (unsigned)TC ? max(t[i], 0) : 0;
+}
+
 // A 16-byte load of K/V page data with the nontemporal hint, for the decode kernel, which reads
 // every K/V byte of a call once: streaming it through the caches rather than keeping it there
 // raises the achieved HBM rate of the 12-stream decode from about 5.6 to 5.9-6.3 TB/s.  (The

@@ -15,7 +15,7 @@ __global__ __launch_bounds__(256) void rows_put_kernel(const RowsArgs a) {
     const int row = blockIdx.x;            // s * R + r
     const int s = row / a.R;
     const int r = row - s * a.R;
-    const int pos = a.seq_len[s] - a.R + r;
+    const int pos = kernel_len(a.seq_len[s], a.max_len) - a.R + r;
     if (pos < 0) return;
     int idx = pos / a.P;
     const int off = pos - idx * a.P;
@@ -129,7 +129,7 @@ __global__ __launch_bounds__(64) void merge_kernel(const MergeArgs a) {
             xe[u][1] = src[1];
         }
     }
-    const int L = a.seq_len[s];
+    const int L = kernel_len(a.seq_len[s], a.max_len);
     const int pos = L - a.R + r;
     float num[8];
 #pragma unroll
@@ -138,19 +138,8 @@ __global__ __launch_bounds__(64) void merge_kernel(const MergeArgs a) {
     if (pos >= 0) {
         // this row reads only the splits holding its own keys [lo_r, pos]: the even pieces of
         // the stream, or the chunks counted from the first chunk any row of the stream sees
-        const int lo_r = a.window > 0 ? max(0, pos - a.window + 1) : 0;
-        int i_begin, n;
-        if (a.even) {
-            const int base = split_base(L, a.R, a.window, a.align);
-            const int piece = split_piece(L, base, a.n_splits, a.align);
-            i_begin = (lo_r - base) / piece;
-            n = min((pos - base) / piece + 1, a.n_splits);
-        } else {
-            const int lo_stream = a.window > 0 ? max(0, L - a.R - a.window + 1) : 0;
-            const int first = lo_stream / a.chunk;
-            i_begin = lo_r / a.chunk - first;
-            n = min(pos / a.chunk - first + 1, a.n_splits);
-        }
+        const SplitSpan sp = row_splits(L, a.R, a.window, pos, a.n_splits, a.chunk, a.even != 0, a.align);
+        const int i_begin = sp.first, n = sp.end;
         if (n - i_begin <= 4 * SG) {
             // one pass (every decode and verify plan here): the partials and their (m, l) are
             // loaded together, before the max is known

@@ -44,7 +44,7 @@ struct MfmaGeom {
     static constexpr int KPT = KT * CB / NT;            // keys per thread per tile (4 or 8)
     static constexpr int UPR = KT / 4;                  // V^T units (4 keys) per channel
     static constexpr int RPS = 32 / UPR;                // channels per 32-unit (256-byte) row
-    static constexpr int TC = 160;                      // cached page-table entries
+    static constexpr int TC = kTableCache;              // cached page-table entries
 };
 
 static_assert(MfmaGeom<128>::KPT == 4 && MfmaGeom<512>::KPT == 8, "thread tiling");
@@ -72,6 +72,7 @@ __device__ __forceinline__ int vt_unit(int ch, int kg) {
 }
 
 int mfma_tile_keys(int D) { return D == 512 ? MfmaGeom<512>::KT : MfmaGeom<128>::KT; }
+int mfma_table_mode(int D, int P, int chunk) { return table_mode(P, chunk, mfma_tile_keys(D), 1); }
 
 bool mfma_supported(int D, int G, int R) {
     return (D == 128 || D == 512) && (G == 4 || G == 8 || G == 12 || G == 16) && R >= 1 && R * G >= 16;
@@ -220,7 +221,7 @@ __global__ __launch_bounds__(256 * KS) void part_mfma_kernel(const PartArgs a) {
     // stream's whole page table fits the cache (a full layer of at most TC pages), its table
     // entries: none of them depends on the stream's length, so they are loaded together with
     // it, and the first K/V loads wait for one round trip to memory rather than two.
-    const bool whole = MODE != 2 && a.ring_pages == 0 && a.stride <= TC;
+    const bool whole = whole_table(MODE, a.ring_pages, a.stride);
     const int Lv = load_uniform_i32(a.seq_len + s);
     bool col_ok[QW];
     int rq[QW], hq[QW];
@@ -250,7 +251,7 @@ __global__ __launch_bounds__(256 * KS) void part_mfma_kernel(const PartArgs a) {
             tv[k] = i < a.stride ? trow[i] : -1;
         }
     }
-    const int L = __builtin_amdgcn_readfirstlane(Lv);
+    const int L = kernel_len(__builtin_amdgcn_readfirstlane(Lv), a.max_len);
     if (whole) {
 #pragma unroll
         for (int k = 0; k < TPT; ++k) {
@@ -262,15 +263,11 @@ __global__ __launch_bounds__(256 * KS) void part_mfma_kernel(const PartArgs a) {
     const int r_first = v0 / G;
     const int r_last = (min(NQ, v0 + M) - 1) / G;
     const int p_first = L - R + r_first, p_last = L - R + r_last;
-    const int lo_stream = W > 0 ? max(0, L - R - W + 1) : 0;
-    const int lo_tile = W > 0 ? max(0, p_first - W + 1) : 0;
     // a split is a chunk of absolute positions; a direct call's one split starts at the tile's
     // first visible key, and its chunk (>= window + R - 1, or >= max_seq_len) then covers every
-    // key the tile's rows see (the bound only matters for lengths beyond max_seq_len: it keeps
-    // the table entries the tile reads within the cached ones)
-    const int c0 = a.direct ? lo_tile : (lo_stream / CH + split) * CH;
-    const int kbeg = max(c0, lo_tile);
-    const int kend = min(c0 + CH, p_last + 1);
+    // key the tile's rows see
+    const KeyRange keys = mfma_keys(L, R, W, CH, split, a.direct != 0, r_first, r_last);
+    const int kbeg = keys.kbeg, kend = keys.kend;
     if (kbeg >= kend) {
         // no row of the tile sees this chunk: nothing to merge; a direct call owns the output
         // of its rows, which are then rows before the start of the stream: zeros
@@ -337,7 +334,7 @@ __global__ __launch_bounds__(256 * KS) void part_mfma_kernel(const PartArgs a) {
         if (MODE == 0) {
             // the whole tile lies in one page
             const int idx = tb / P;
-            const int pg = max(t_lds[idx - idx0], 0);
+            const int pg = cached_page<TC>(t_lds, idx - idx0);
             const size_t base = (size_t)pg * page_elems + head_off + (size_t)(tb - idx * P + KPT * kq) * D + 8 * kc;
 #pragma unroll
             for (int u = 0; u < KPT; ++u) r[u] = ld16(pages + base + (size_t)u * D);
@@ -349,7 +346,7 @@ __global__ __launch_bounds__(256 * KS) void part_mfma_kernel(const PartArgs a) {
                 const int off = j - idx * P;
                 int pg;
                 if (MODE == 1) {
-                    pg = t_lds[idx - idx0];
+                    pg = cached_page<TC>(t_lds, idx - idx0);
                 } else {
                     if (a.ring_pages) idx %= a.ring_pages;
                     const int tp = trow[min(idx, a.stride - 1)];
@@ -729,13 +726,11 @@ template <int D, int G, int QW, int KS, bool NTL>
 static hipError_t launch_dgq(const PartArgs &a, hipStream_t st) {
     using Geo = MfmaGeom<D>;
     const dim3 grid(8 * a.per_xcd);
-    const bool cached = (a.chunk + Geo::KT) / a.P + 2 <= Geo::TC;
-    if (cached && a.P % Geo::KT == 0)
-        hipLaunchKernelGGL((part_mfma_kernel<D, G, QW, 0, KS, NTL>), grid, dim3(256 * KS), 0, st, a);
-    else if (cached)
-        hipLaunchKernelGGL((part_mfma_kernel<D, G, QW, 1, KS, NTL>), grid, dim3(256 * KS), 0, st, a);
-    else
-        hipLaunchKernelGGL((part_mfma_kernel<D, G, QW, 2, KS, NTL>), grid, dim3(256 * KS), 0, st, a);
+    switch (table_mode(a.P, a.chunk, Geo::KT, 1)) {
+        case 0: hipLaunchKernelGGL((part_mfma_kernel<D, G, QW, 0, KS, NTL>), grid, dim3(256 * KS), 0, st, a); break;
+        case 1: hipLaunchKernelGGL((part_mfma_kernel<D, G, QW, 1, KS, NTL>), grid, dim3(256 * KS), 0, st, a); break;
+        default: hipLaunchKernelGGL((part_mfma_kernel<D, G, QW, 2, KS, NTL>), grid, dim3(256 * KS), 0, st, a); break;
+    }
     return hipGetLastError();
 }
 

@@ -38,7 +38,7 @@ struct ValuGeom {
     static constexpr int QL = 64 / NB;        // lanes per key in the QK stage
     static constexpr int SEG = D / QL;        // channels per QK lane
     static constexpr int RS = D + 8;          // LDS row stride (bf16 elements)
-    static constexpr int TC = 160;            // page-table entries cached per chunk
+    static constexpr int TC = kTableCache;    // page-table entries cached per chunk
 };
 
 // Splits of one call, a function of the call's shape only.  Each stream is cut into n_splits
@@ -95,7 +95,7 @@ struct BatchLoader {
         if constexpr (MODE == 0) {
             // the whole batch lies in one page: one lookup
             const int idx = b / P;
-            const int pg = max(t_lds[idx - idx0], 0);
+            const int pg = cached_page<ValuGeom<D>::TC>(t_lds, idx - idx0);
             const size_t base = (size_t)pg * page_elems + head_off + (size_t)(b - idx * P + lrow) * D;
 #pragma unroll
             for (int i = 0; i < NS; ++i) {
@@ -110,7 +110,7 @@ struct BatchLoader {
             int off = j0 - idx * P;
 #pragma unroll
             for (int i = 0; i < NS; ++i) {
-                const int pg = max(t_lds[idx - idx0], 0);
+                const int pg = cached_page<ValuGeom<D>::TC>(t_lds, idx - idx0);
                 const size_t e = (size_t)pg * page_elems + head_off + (size_t)off * D;
                 kr[i] = stream_load(k_pages + e);
                 vr[i] = stream_load(v_pages + e);
@@ -144,15 +144,12 @@ constexpr int valu_vw() { return NQ % 2 == 0 && NQ <= 8 ? 2 : 4; }
 template <int NQ>
 constexpr int valu_waves() { return NQ / valu_vw<NQ>(); }
 
-// Load modes, fixed per launch from P: 0 when P is a multiple of the batch, 1 when rows
-// straddle pages but the chunk's table entries fit the LDS cache, 2 for tiny pages.
+// Load modes, fixed per launch from P (table_mode over batches of NB keys): 0 when P is a
+// multiple of the batch, 1 when rows straddle pages but the chunk's table entries fit the LDS
+// cache, 2 for tiny pages.
 template <int D>
 int valu_mode(int P, int chunk) {
-    using Geo = ValuGeom<D>;
-    const bool cached = (chunk + Geo::NB) / P + 2 <= Geo::TC;
-    if (cached && P % Geo::NB == 0) return 0;
-    if (cached && Geo::RPI <= P) return 1;
-    return 2;
+    return table_mode(P, chunk, ValuGeom<D>::NB, ValuGeom<D>::RPI);
 }
 
 // At d 128 with 8 query vectors and one lookup per batch (MODE 0, pages a multiple of the
@@ -197,7 +194,7 @@ __global__ __launch_bounds__(64 * valu_waves<NQ>()) __attribute__((amdgpu_waves_
     constexpr int QN = NQ * (D / 8);                          // 16-byte query pieces
     constexpr int QPT = (QN + 64 * NW - 1) / (64 * NW);       // per thread
     constexpr int TPT = (TC + 64 * NW - 1) / (64 * NW);       // table entries per thread
-    const bool whole = MODE != 2 && a.ring_pages == 0 && a.stride <= TC;
+    const bool whole = whole_table(MODE, a.ring_pages, a.stride);
     const int Lv = load_uniform_i32(a.seq_len + s);
     u32x4 qv[QPT];
     int tv[TPT];
@@ -216,7 +213,7 @@ __global__ __launch_bounds__(64 * valu_waves<NQ>()) __attribute__((amdgpu_waves_
             tv[k] = i < a.stride ? trow[i] : -1;
         }
     }
-    const int L = __builtin_amdgcn_readfirstlane(Lv);
+    const int L = kernel_len(__builtin_amdgcn_readfirstlane(Lv), a.max_len);
 #pragma unroll
     for (int k = 0; k < QPT; ++k) {
         const int i = tid + k * 64 * NW;
@@ -234,17 +231,10 @@ __global__ __launch_bounds__(64 * valu_waves<NQ>()) __attribute__((amdgpu_waves_
     }
 
     const int W = a.window;
-    const int lo = W > 0 ? max(0, L - R - W + 1) : 0;
     if (L <= 0 || split >= a.n_splits) return;
-    const int base = split_base(L, R, W, NB);
-    const int piece = split_piece(L, base, a.n_splits, NB);
-    const int c0 = base + split * piece;
-    if (c0 >= L) return;
-    const int kbeg = max(c0, lo);
-    // a piece never runs past the host's longest piece (a.chunk, from max_seq_len): a device
-    // length above max_seq_len is a caller error, and this bound keeps its loads inside the
-    // chunk's cached table entries (and so inside the pool) rather than past them
-    const int kend = min(min(c0 + piece, c0 + a.chunk), L);
+    const KeyRange keys = valu_keys(L, R, W, a.n_splits, NB, a.chunk, split);
+    if (keys.c0 >= L) return;
+    const int kbeg = keys.kbeg, kend = keys.kend;
 
     const int lrow = lane / LPR;            // row inside a group of RPI rows (load and PV)
     const int lch = lane - lrow * LPR;      // 16-byte piece of the row
@@ -279,7 +269,7 @@ __global__ __launch_bounds__(64 * valu_waves<NQ>()) __attribute__((amdgpu_waves_
             const int off = (L - 1) - idx * P;
             if (a.ring_pages) idx %= a.ring_pages;
             // with the whole table cached, its entry is already in LDS (validated, -1 if bad)
-            const int pg = whole ? t_lds[idx] : (idx < a.stride ? trow[idx] : -1);
+            const int pg = idx < a.stride ? (whole ? t_lds[idx] : trow[idx]) : -1;
             if ((unsigned)pg < (unsigned)a.num_pages) {
                 const size_t dst = (size_t)pg * page_elems + head_off + (size_t)off * D;   // head_off has the lane's 8 channels
                 *reinterpret_cast<u32x4 *>(const_cast<uint16_t *>(a.k_pages) + dst) =
@@ -476,6 +466,21 @@ __global__ __launch_bounds__(64 * valu_waves<NQ>()) __attribute__((amdgpu_waves_
         dst[1] = make_float4(acc[i][4], acc[i][5], acc[i][6], acc[i][7]);
         if (lch == 0) *reinterpret_cast<float2 *>(a.ws_ml + slot * 2) = make_float2(m_run[i], l_tot[i]);
     }
+}
+
+int valu_batch_keys(int D) { return D == 512 ? ValuGeom<512>::NB : ValuGeom<128>::NB; }
+int valu_rows_per_load(int D) { return D == 512 ? ValuGeom<512>::RPI : ValuGeom<128>::RPI; }
+int valu_table_mode(int D, int P, int chunk) { return D == 512 ? valu_mode<512>(P, chunk) : valu_mode<128>(P, chunk); }
+template <int NQ>
+static void load_shape(int *waves, int *slots) {
+    *waves = valu_waves<NQ>();
+    *slots = BatchLoader<128, valu_waves<NQ>()>::NS;
+}
+void valu_load_shape(int NQ, int *waves, int *slots_per_wave) {
+    *waves = *slots_per_wave = 0;
+    if (NQ == 4) load_shape<4>(waves, slots_per_wave);
+    if (NQ == 8) load_shape<8>(waves, slots_per_wave);
+    if (NQ == 12) load_shape<12>(waves, slots_per_wave);
 }
 
 bool valu_supported(int D, int G, int NQ) {
