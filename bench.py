@@ -5,10 +5,10 @@ stream written into its page slot, then the split-context part kernel and the me
 contexts uniform in [32768, 40960] with 8 KV / 64 query heads, head_dim 128, bf16, pages of
 512 shuffled over the pool.  Inputs are resident in HBM before the timed region starts.
 
-Before the timed region the step runs until the part kernel's time has settled (the medians of
-three windows of ten launches within 2 % of each other, or a time cap), independent of
---warmup: the first tens of milliseconds of sustained load run at a lower clock.  The settle is
-reported on its own.
+Before the timed region the step runs until the part kernel's time has settled (at least 150
+launches, then the medians of three windows of ten launches within 2 % of each other, or a time
+cap), independent of --warmup: the first tens of milliseconds of sustained load run at a lower
+clock.  The settle is reported on its own.
 
 Prints one JSON line: `value` is K/V bytes read per step over the measured step time (GB/s,
 whole job), `roofline` compares the part kernel's average duration (HIP events recorded on
@@ -157,8 +157,10 @@ def run_steps(setup, steps, torch, binding):
     return (t1 - t0) * 1e3 / steps, [starts[i].elapsed_time(stops[i]) for i in range(steps)]
 
 
-def settle(setup, torch, binding, max_ms, window=10, windows=3, tol=1.02):
-    """Step in windows of `window` launches until the part kernel's median over each of the last
+def settle(setup, torch, binding, max_ms, window=10, windows=3, tol=1.02, min_steps=150):
+    """Step in windows of `window` launches, at least min_steps launches (the shader clock is
+    still ramping 40-80 launches into the load on some boxes, by 5-10 % per launch, in steps
+    that can look flat over 30 launches), until the part kernel's median over each of the last
     `windows` windows agree within `tol` (max / min: the level has stopped moving), or until
     max_ms of stepping; returns the record of the phase."""
     times, meds = [], []
@@ -169,14 +171,14 @@ def settle(setup, torch, binding, max_ms, window=10, windows=3, tol=1.02):
         times += pm
         meds.append(sorted(pm)[window // 2])
         last = meds[-windows:]
-        if len(last) == windows and max(last) <= tol * min(last):
+        if len(times) >= min_steps and len(last) == windows and max(last) <= tol * min(last):
             reached = True
             break
         if (time.perf_counter() - t0) * 1e3 > max_ms:
             break
     return {"steps": len(times), "wall_ms": round((time.perf_counter() - t0) * 1e3, 1), "reached": reached,
-            "rule": f"medians of the last {windows} windows of {window} part-kernel launches within "
-                    f"{round((tol - 1) * 100)} %, capped at {max_ms:.0f} ms",
+            "rule": f"at least {min_steps} launches, then medians of the last {windows} windows of {window} "
+                    f"part-kernel launches within {round((tol - 1) * 100)} %, capped at {max_ms:.0f} ms",
             "part_us": [round(x * 1e3, 1) for x in times[:400]]}
 
 
