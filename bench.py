@@ -198,27 +198,30 @@ def flush_buffer(torch):
 
 def cold_calls(fn, iters, torch, flush, part=False, binding=None):
     """Event-timed calls of fn, each preceded by a FLUSH_BYTES write that evicts L2 and MALL;
-    with part, also the part kernel alone (events the library records around it).  Returns
-    (call ms list, part ms list or None)."""
+    with part, also the part kernel alone (events the library records around it), in calls of
+    their own that alternate with the whole-call ones: event records inside a timed call would
+    add their own cost to it (about 7 µs for the two around the part kernel).  Returns (call ms
+    list, part ms list or None)."""
     ms, pms = [], []
     for _ in range(iters):
         flush.fill_(1)
         a = torch.cuda.Event(enable_timing=True)
         b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn()
+        b.record()
+        torch.cuda.synchronize()
+        ms.append(a.elapsed_time(b))
         if part:
+            flush.fill_(1)
             pa = torch.cuda.Event(enable_timing=True)
             pb = torch.cuda.Event(enable_timing=True)
             pa.record()
             pb.record()
             binding.set_part_events(pa.cuda_event, pb.cuda_event)
-        a.record()
-        fn()
-        b.record()
-        if part:
+            fn()
             binding.set_part_events(None, None)
-        torch.cuda.synchronize()
-        ms.append(a.elapsed_time(b))
-        if part:
+            torch.cuda.synchronize()
             pms.append(pa.elapsed_time(pb))
     return ms, (pms if part else None)
 
