@@ -10,13 +10,16 @@
   write and the fused row write + decode are compared with the oracle, at the headline geometry
   (pages of 512, one lookup per tile) and at head dim 512 over pages of 37 (lookups per row).
 
-Every output is compared in full with the oracle.
+Every output is compared in full with the oracle.  The long stream's pool is also compared byte
+for byte with the oracle's scatter of its history before it is attended, so that a wrong
+output can be told apart from wrong pages.
 """
 import numpy as np
 import pytest
 import torch
 
-from gpu_support import (assert_close, attend, oracle_for, oracle_from_history, pool_bits, remember, say)
+from gpu_support import (assert_close, attend, expected_pool, oracle_for, oracle_from_history, pool_bits, remember,
+                         say)
 from paged_kv_cache_rows_amd import binding, staging, workloads
 
 pytestmark = pytest.mark.gpu
@@ -29,6 +32,14 @@ def _long(P, rows):
                               lengths=[LONG], spare_frac=0.02, min_spares=2, seed=91)
 
 
+def _pool_is_the_history(c):
+    kb, vb = expected_pool(c)
+    ka, va = pool_bits(c)
+    bad_k = np.argwhere((ka != kb).any(axis=(1, 2, 3))).ravel()
+    bad_v = np.argwhere((va != vb).any(axis=(1, 2, 3))).ravel()
+    assert bad_k.size == 0 and bad_v.size == 0, f"pages differing from the oracle's scatter: K {bad_k[:8]}, V {bad_v[:8]}"
+
+
 @pytest.mark.parametrize("P", [64, 37])
 def test_decode_over_262144_keys(P):
     w = _long(P, 1)
@@ -37,6 +48,7 @@ def test_decode_over_262144_keys(P):
     ks, vs = workloads.kv_history(w)
     staging.write_history(c, ks, vs)
     remember(c, ks, vs)
+    _pool_is_the_history(c)
     q = workloads.queries(w).cuda()
     out = attend("decode", c, q)
     assert torch.isfinite(out.float()).all()
@@ -50,6 +62,7 @@ def test_verify_over_262144_keys():
     ks, vs = workloads.kv_history(w)
     staging.write_history(c, ks, vs)
     remember(c, ks, vs)
+    _pool_is_the_history(c)
     q = workloads.queries(w).cuda()
     out = attend("verify", c, q)
     again = attend("verify", c, q)
