@@ -43,6 +43,12 @@ extern "C" {
 
 #define KVPAGED_ABI_VERSION 1
 
+/* The longest stream a call may describe (kv_layout.max_seq_len) and the widest sliding window
+ * (kv_attn_args.window): 2^29 positions.  Within them every position, key range, chunk end and
+ * piece length the kernels and the planning form stays below 2^31 in 32-bit ints; a larger
+ * value is refused with KV_E_ARG. */
+#define KV_MAX_SEQ_LEN (1 << 29)
+
 typedef enum kv_status {
     KV_OK = 0,
     KV_E_ARG = -1,        /* a null pointer, a negative or inconsistent size, a bad stream id */
@@ -83,7 +89,8 @@ typedef struct kv_layout {
                                   rows; the call's rows sit at positions L-R .. L-1, and rows at
                                   negative positions (R > L) are not written and see no key */
     int32_t max_seq_len;       /* host: an upper bound of seq_len over the call (sizes grids and
-                                  the workspace).  A larger device length is a caller error: the
+                                  the workspace), rows <= max_seq_len <= KV_MAX_SEQ_LEN.  A
+                                  larger device length is a caller error: the
                                   kernels read it as max_seq_len, so every access stays inside
                                   the table and workspace planned for the call, and KVP_CHECK=1
                                   refuses it before launch */
@@ -98,7 +105,8 @@ typedef struct kv_attn_args {
     void *out;               /* device bf16 [S][R][Hq][D], 16-byte aligned, written in full */
     int32_t num_q_heads;     /* Hq, a multiple of Hkv; query head h reads KV head h / (Hq/Hkv) */
     float scale;             /* score scale; 0 means 1/sqrt(D) */
-    int32_t window;          /* 0: full causal; W > 0: row at position p sees keys p-W+1 .. p */
+    int32_t window;          /* 0: full causal; W > 0: row at position p sees keys p-W+1 .. p
+                                (W <= KV_MAX_SEQ_LEN) */
     void *workspace;         /* device scratch, >= paged_attn_workspace_size() bytes, 256-byte
                                 aligned; its contents on entry do not matter */
     size_t workspace_bytes;

@@ -285,6 +285,7 @@ def decode_put(pool, q, table, seq_len, max_seq_len, k_new: torch.Tensor, v_new:
 
 
 STATIC_SCRATCH_BYTES = 32 << 20     # KV_STATIC_SCRATCH_BYTES
+KV_MAX_SEQ_LEN = 1 << 29            # the longest max_seq_len and widest window a call may give
 
 
 def decode_put_static(pool, q, table, seq_len, max_seq_len, k_new: torch.Tensor, v_new: torch.Tensor,

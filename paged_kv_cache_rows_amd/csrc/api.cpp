@@ -64,6 +64,8 @@ kv_status check_layout(const kv_pool *pool, const kv_layout *lay, const char *wh
     if (!lay->page_table || !lay->seq_len) return fail(KV_E_ARG, "%s: page_table or seq_len is null", who);
     if (lay->max_seq_len < lay->rows)
         return fail(KV_E_ARG, "%s: max_seq_len %d < rows %d", who, lay->max_seq_len, lay->rows);
+    if (lay->max_seq_len > KV_MAX_SEQ_LEN)
+        return fail(KV_E_ARG, "%s: max_seq_len %d > %d", who, lay->max_seq_len, KV_MAX_SEQ_LEN);
     if (lay->ring_pages < 0) return fail(KV_E_ARG, "%s: ring_pages %d < 0", who, lay->ring_pages);
     const int need = lay->ring_pages ? lay->ring_pages : ceil_div(lay->max_seq_len, pool->page_size);
     if (lay->table_stride < need)
@@ -123,7 +125,8 @@ kv_status make_plan(const kv_pool *pool, const kv_layout *lay, const kv_attn_arg
     if (a->num_q_heads < 1 || a->num_q_heads % pool->num_kv_heads != 0)
         return fail(KV_E_ARG, "%s: num_q_heads %d is not a positive multiple of num_kv_heads %d", who,
                     a->num_q_heads, pool->num_kv_heads);
-    if (a->window < 0) return fail(KV_E_ARG, "%s: window %d < 0", who, a->window);
+    if (a->window < 0 || a->window > KV_MAX_SEQ_LEN)
+        return fail(KV_E_ARG, "%s: window %d outside [0, %d]", who, a->window, KV_MAX_SEQ_LEN);
     if (!(a->scale >= 0.f) || std::isinf(a->scale)) return fail(KV_E_ARG, "%s: scale must be finite and >= 0", who);
     if (lay->ring_pages && a->window <= 0)
         return fail(KV_E_ARG, "%s: a ring layer needs a sliding window", who);

@@ -16,10 +16,16 @@
 //     row's keys;
 //   * the fused decode row write finds the page of position L - 1;
 //   * a device length above max_seq_len is read as max_seq_len.
+// Streams at the longest length a call may describe (KV_MAX_SEQ_LEN) are checked for their
+// ranges and merge spans only (no row walk): the checker is built with the signed-overflow
+// check of UndefinedBehaviorSanitizer, so any 32-bit overflow in the shared range functions
+// aborts it.
 // `--plant merge` drops the last split of every merge span and `--plant cache` shrinks the
-// checker's idea of the table cache by one entry: both must be reported.
+// checker's idea of the table cache by one entry: both must be reported.  `--plant overflow`
+// feeds split_piece a length past the limit: the sanitizer must stop the run.
 //
 // Exit status 0 and a line "violations 0" when every check holds.
+#include "../include/kvpaged.h"
 #include "internal.h"
 
 #include <algorithm>
@@ -41,6 +47,7 @@ struct Shape {
 };
 
 std::string plant;
+bool walk_rows = true;      // false: ranges and merge spans only (streams too long to walk)
 long long violations = 0, wg_checked = 0, rows_checked = 0, lengths_checked = 0;
 long long fallbacks = 0;   // rows read through an absent entry (page 0), none of them used
 long long outside = 0;     // lookups whose index falls outside the cache (the guard's case)
@@ -52,15 +59,19 @@ void report(const Shape &c, int L, const char *what, long long a, long long b) {
                     c.D, c.G, c.R, c.S, c.P, c.max_len, c.window, c.ring, c.extra_stride, L, a, b);
 }
 
-// The stream's table: entries [0, stride), pages of a pool of num_pages.
+// The stream's table: entries [0, stride), pages of a pool of num_pages (entries are only
+// filled in when rows are walked).
 struct Table {
     std::vector<int32_t> e;
     int num_pages;
+    int stride;
 };
 
 Table make_table(int stride, uint32_t seed) {
     Table t;
     t.num_pages = 2 * stride + 5;
+    t.stride = stride;
+    if (!walk_rows) return t;
     t.e.resize(stride);
     for (int i = 0; i < stride; ++i) t.e[i] = (int32_t)((seed + 7919u * (uint32_t)i) % (uint32_t)t.num_pages);
     return t;
@@ -79,7 +90,7 @@ int true_page(const Shape &c, const Table &t, int j) {
 // the pool.
 std::vector<int> cached_entries(const Shape &c, const Table &t, bool whole, int idx0) {
     std::vector<int> v(kTableCache);
-    const int stride = (int)t.e.size();
+    const int stride = t.stride;
     for (int i = 0; i < kTableCache; ++i) {
         int idx = whole ? i : idx0 + i;
         if (!whole && c.ring) idx %= c.ring;
@@ -107,7 +118,7 @@ Lookup cached_page(const std::vector<int> &t, int i) {
 
 Lookup global_page(const Shape &c, const Table &t, int idx) {
     if (c.ring) idx %= c.ring;
-    const int stride = (int)t.e.size();
+    const int stride = t.stride;
     const int tp = t.e[std::min(idx, stride - 1)];
     if (idx < stride && tp >= 0 && tp < t.num_pages) return {tp, false};
     return {0, true};
@@ -139,7 +150,7 @@ bool tiles_exactly(std::vector<std::pair<int, int>> iv, int a, int b) {
     std::vector<std::pair<int, int>> ne;
     for (const auto &x : iv)
         if (x.first < x.second) ne.push_back(x);
-    std::sort(ne.begin(), ne.end());
+    if (!std::is_sorted(ne.begin(), ne.end())) std::sort(ne.begin(), ne.end());
     int at = a;
     for (const auto &x : ne) {
         if (x.first != at) return false;
@@ -154,7 +165,7 @@ void check_valu(const Shape &c, const CallPlan &p, const Table &t, int Ldev) {
     if (L <= 0) return;
     const int NB = valu_batch_keys(c.D), RPI = valu_rows_per_load(c.D);
     const int mode = valu_table_mode(c.D, c.P, p.chunk);
-    const int stride = (int)t.e.size();
+    const int stride = t.stride;
     const bool whole = whole_table(mode, c.ring, stride);
     int NW, NS;
     valu_load_shape(c.R * c.G, &NW, &NS);
@@ -173,6 +184,7 @@ void check_valu(const Shape &c, const CallPlan &p, const Table &t, int Ldev) {
         if (k.kbeg >= k.kend) report(c, L, "written piece with no keys", k.kbeg, k.kend);
         if (k.kend - k.c0 > p.chunk) report(c, L, "piece longer than the planned chunk", k.kend - k.c0, p.chunk);
         cover.push_back({k.kbeg, k.kend});
+        if (!walk_rows) continue;
         const int b_first = (k.kbeg / NB) * NB;
         const int nb = (k.kend - b_first + NB - 1) / NB;
         const int idx0 = whole ? 0 : b_first / c.P;
@@ -239,7 +251,7 @@ void check_mfma(const Shape &c, const CallPlan &p, const Table &t, int Ldev) {
     if (L <= 0) return;
     const int KT = mfma_tile_keys(c.D);
     const int mode = mfma_table_mode(c.D, c.P, p.chunk);
-    const int stride = (int)t.e.size();
+    const int stride = t.stride;
     const bool whole = whole_table(mode, c.ring, stride);
     const int NQ = c.R * c.G, M = 64 * p.mp.qw;
     if (p.chunk % KT != 0) report(c, L, "chunk not a whole number of tiles", p.chunk, KT);
@@ -261,6 +273,7 @@ void check_mfma(const Shape &c, const CallPlan &p, const Table &t, int Ldev) {
             written[split] = 1;
             if (k.kend - k.c0 > p.chunk) report(c, L, "chunk overrun", k.kend - k.c0, p.chunk);
             cover.push_back({k.kbeg, k.kend});
+            if (!walk_rows) continue;
             const int kt_first = (k.kbeg / KT) * KT;
             const int nt = (k.kend - kt_first + KT - 1) / KT;
             const int idx0 = whole ? 0 : kt_first / c.P;
@@ -311,15 +324,19 @@ void check_shape(const Shape &c, std::mt19937 &rng) {
     }
     const int need = c.ring ? c.ring : (int)(((int64_t)c.max_len + c.P - 1) / c.P);
     const Table t = make_table(need + c.extra_stride, rng());
-    std::vector<int> Ls = {0, 1, c.R - 1, c.R, c.R + 1, c.P - 1, c.P, c.P + 1, 2 * c.P + 3, 63, 64, 65,
-                           c.max_len / 2, c.max_len - 1, c.max_len, c.max_len + 1, 2 * c.max_len + 7,
-                           INT_MAX, -3};
-    if (c.window > 0) {
-        Ls.push_back(c.window + c.R - 1);
-        Ls.push_back(c.window + c.R);
+    std::vector<int> Ls;
+    if (!walk_rows) {
+        Ls = {c.R, c.max_len / 3 + 37, c.max_len - 1, c.max_len, c.max_len + 1, INT_MAX};
+    } else {
+        Ls = {0, 1, c.R - 1, c.R, c.R + 1, c.P - 1, c.P, c.P + 1, 2 * c.P + 3, 63, 64, 65,
+              c.max_len / 2, c.max_len - 1, c.max_len, c.max_len + 1, 2 * c.max_len + 7, INT_MAX, -3};
+        if (c.window > 0) {
+            Ls.push_back(c.window + c.R - 1);
+            Ls.push_back(c.window + c.R);
+        }
+        std::uniform_int_distribution<int> u(1, c.max_len);
+        for (int i = 0; i < 4; ++i) Ls.push_back(u(rng));
     }
-    std::uniform_int_distribution<int> u(1, c.max_len);
-    for (int i = 0; i < 4; ++i) Ls.push_back(u(rng));
     for (int L : Ls) {
         ++lengths_checked;
         if (p.mfma) check_mfma(c, p, t, L);
@@ -370,6 +387,22 @@ int main(int argc, char **argv) {
         shapes.push_back({512, gr[0], gr[1], 1, 8, 37, 65536, 4096, 0, 0});
     }
     for (const Shape &c : shapes) check_shape(c, rng);
+    // the longest streams a call may describe, and the widest window: ranges and merge spans
+    walk_rows = false;
+    std::vector<Shape> limit;
+    const int GRL[][2] = {{8, 1}, {4, 3}, {8, 4}, {16, 4}, {8, 256}};
+    for (int D : Ds)
+        for (const auto &gr : GRL)
+            for (int P : {37, 512})
+                for (int W : {0, 1, 4096, KV_MAX_SEQ_LEN - 1, KV_MAX_SEQ_LEN})
+                    limit.push_back({D, gr[0], gr[1], 12, 8, P, KV_MAX_SEQ_LEN, W, 0, 0});
+    for (const Shape &c : limit) check_shape(c, rng);
+    shapes.insert(shapes.end(), limit.begin(), limit.end());
+    if (plant == "overflow") {
+        volatile int big = INT_MAX - 3;
+        std::printf("planted: split_piece over %d positions\n", (int)big);
+        std::printf("piece %d\n", split_piece(big, 0, 8, 64));
+    }
     std::printf("shapes %zu lengths %lld workgroups %lld rows %lld absent-entry rows %lld outside-cache lookups %lld "
                 "violations %lld\n",
                 shapes.size(), lengths_checked, wg_checked, rows_checked, fallbacks, outside, violations);

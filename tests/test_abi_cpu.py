@@ -229,6 +229,9 @@ def _args(Hq=16, window=0, ws=0x50000, nbytes=1 << 30, scale=0.0, q=0x60000, out
     ("paged_attn_decode", _layout(ring=2), _args(), binding.KV_E_ARG),         # ring without a window
     ("paged_attn_decode", _layout(ring=2), _args(window=200), binding.KV_E_ARG),  # ring 128 < window
     ("paged_attn_verify", _layout(max_len=3, R=4), _args(), binding.KV_E_ARG),   # R > max_seq_len
+    ("paged_attn_decode", _layout(max_len=binding.KV_MAX_SEQ_LEN + 1, stride=(1 << 23) + 2), _args(),
+     binding.KV_E_ARG),                                                        # stream past the limit
+    ("paged_attn_decode", _layout(), _args(window=binding.KV_MAX_SEQ_LEN + 1), binding.KV_E_ARG),  # window past it
 ])
 @host_only
 def test_attention_refuses_before_launch(lib, entry, lay, args, status):
@@ -425,3 +428,29 @@ def test_static_scratch_size_matches_the_header():
     text = open(HEADER).read()
     m = re.search(r"#define KV_STATIC_SCRATCH_BYTES \((\d+)u << (\d+)\)", text)
     assert m and int(m.group(1)) << int(m.group(2)) == binding.STATIC_SCRATCH_BYTES
+
+
+@pytest.mark.parametrize("D,Hq,R", [(128, 16, 1), (128, 32, 4), (512, 32, 4)])
+def test_the_longest_stream_and_widest_window_are_planned(lib, D, Hq, R):
+    # at KV_MAX_SEQ_LEN (and a window as wide) the workspace size is computed without refusal;
+    # one position more is refused
+    d = binding.PoolDesc(8, 64, 4, D, 2, 0x10000, 0x20000, None)
+    h = ctypes.c_void_p()
+    assert lib.kv_pool_create(ctypes.byref(d), ctypes.byref(h)) == 0
+    n = ctypes.c_size_t()
+    top = binding.KV_MAX_SEQ_LEN
+    stride = top // 64
+    for window in (0, top):
+        st = lib.paged_attn_workspace_size(h, ctypes.byref(_layout(R=R, stride=stride, max_len=top)),
+                                           ctypes.byref(_args(Hq=Hq, window=window)), ctypes.byref(n))
+        assert st == binding.KV_OK and n.value > 0, lib.kv_last_error()
+    st = lib.paged_attn_workspace_size(h, ctypes.byref(_layout(R=R, stride=stride + 1, max_len=top + 1)),
+                                       ctypes.byref(_args(Hq=Hq)), ctypes.byref(n))
+    assert st == binding.KV_E_ARG
+    lib.kv_pool_destroy(h)
+
+
+def test_max_seq_len_limit_matches_the_header():
+    text = open(os.path.join(ROOT, "include", "kvpaged.h")).read()
+    m = re.search(r"#define KV_MAX_SEQ_LEN \(1 << (\d+)\)", text)
+    assert m and 1 << int(m.group(1)) == binding.KV_MAX_SEQ_LEN

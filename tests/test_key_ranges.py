@@ -4,7 +4,10 @@ tests/key_ranges_check.cpp is linked with the library's own host objects (its la
 uses the range, lookup-mode and merge-span functions the kernels call.  It walks the load steps
 of every workgroup for about 900 call shapes and 22,000 device lengths, among them lengths
 above max_seq_len (caller errors, which the kernels read as max_seq_len) and full layers of
-exactly as many pages as the kernels cache.  Two planted mistakes must be reported.
+exactly as many pages as the kernels cache; at the longest stream and widest window a call may
+describe (KV_MAX_SEQ_LEN) it checks the ranges and merge spans of every workgroup.  It is built
+with the signed-overflow check of UndefinedBehaviorSanitizer, so a 32-bit overflow in those
+functions stops it.  Three planted mistakes must be reported.
 """
 import os
 import re
@@ -29,7 +32,8 @@ def checker(tmp_path_factory):
     if not all(os.path.exists(o) for o in objs):
         build.build()
     exe = str(tmp_path_factory.mktemp("ranges") / "key_ranges_check")
-    cc = subprocess.run(["g++", "-std=c++17", "-O2", "-Wall", "-D__HIP_PLATFORM_AMD__", "-I/opt/rocm/include",
+    cc = subprocess.run(["g++", "-std=c++17", "-O2", "-Wall", "-fsanitize=signed-integer-overflow",
+                         "-fno-sanitize-recover=all", "-D__HIP_PLATFORM_AMD__", "-I/opt/rocm/include",
                          f"-I{build.CSRC}", SRC, *objs, "-L/opt/rocm/lib", "-lamdhip64",
                          "-Wl,-rpath,/opt/rocm/lib", "-o", exe], capture_output=True, text=True)
     assert cc.returncode == 0, cc.stderr[-4000:]
@@ -47,7 +51,7 @@ def _run(exe, *args):
 def test_every_workgroup_reads_its_own_pages_and_the_pieces_tile_the_keys(checker):
     r, (shapes, lengths, wgs, rows, absent, outside, bad) = _run(checker)
     assert bad == 0 and r.returncode == 0, r.stdout[-3000:]
-    assert shapes > 800 and lengths > 20000 and wgs > 100000 and rows > 10**8
+    assert shapes > 1000 and lengths > 20000 and wgs > 10**7 and rows > 10**8
     # the last load step of a full layer of exactly the cached number of pages (pages of 37 or
     # 100 keys) looks up entries past the cache: those rows must read an absent page, not LDS
     # beyond the table
@@ -59,3 +63,9 @@ def test_every_workgroup_reads_its_own_pages_and_the_pieces_tile_the_keys(checke
 def test_planted_mistakes_are_reported(checker, plant, message):
     r, (*_, bad) = _run(checker, "--plant", plant)
     assert r.returncode == 1 and bad > 0 and message in r.stdout, r.stdout[-2000:]
+
+
+def test_an_overflow_in_the_range_functions_stops_the_checker(checker):
+    r = subprocess.run([checker, "--plant", "overflow"], capture_output=True, text=True, timeout=300)
+    assert r.returncode != 0 and "signed integer overflow" in r.stderr and "internal.h" in r.stderr, \
+        (r.returncode, r.stderr[-2000:])
