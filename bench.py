@@ -333,10 +333,10 @@ def cold_record(ms, kv_bytes, flops=None, part_ms=None):
 
 
 def other_workloads(torch, binding, staging, workloads, flush, cases):
-    """The tiny decode, the verify window (causal and as draft trees), the wide-head pair and
-    the prompt chunks: warm GPU time per call (HIP graph replays; inputs stay in the caches)
-    and cold time per call (a 1 GiB flush before each call, HIP events around it).  Appends to
-    `cases` what the oracle leg needs to check each workload's output."""
+    """The tiny decode, the verify window (causal and as draft trees), the wide-head pair, the
+    head-dim-256 pair and the prompt chunks: warm GPU time per call (HIP graph replays; inputs
+    stay in the caches) and cold time per call (a 1 GiB flush before each call, HIP events
+    around it).  Appends to `cases` what the oracle leg needs to check each workload's output."""
     import numpy as np
     res = {}
     iters = 20
@@ -421,6 +421,32 @@ def other_workloads(torch, binding, staging, workloads, flush, cases):
                   "window": 0, "out": o0.clone()})
     cases.append({"name": "wide_head_verify4_9000", "q": q1, "ks": ks[1:], "vs": vs[1:], "lengths": c.lengths[1:],
                   "window": 0, "out": o1.clone()})
+
+    # head dim 256: 4 streams x 16,384 keys, 4 KV heads x GQA 8, pages of 512; a decode (VALU)
+    # and a 4-row verify window (MFMA), 268 MB of K/V
+    w = workloads.Workload("head_dim_256", streams=4, kv_heads=4, group=8, head_dim=256, page_size=512, rows=4,
+                           lengths=[16384] * 4, spare_frac=0.10, seed=1006)
+    c = staging.make_cache(w, order=workloads.free_order(w.pool_pages, 3007))
+    ks, vs = workloads.kv_history(w, device="cuda")
+    staging.write_history(c, ks, vs)
+    qd = workloads.normal_bf16((4, 1, w.q_heads, 256), 4104, "cuda")
+    qv = workloads.normal_bf16((4, 4, w.q_heads, 256), 4105, "cuda")
+    od, ov = torch.empty_like(qd), torch.empty_like(qv)
+    calld = lambda: binding.decode(c.pool, qd, c.table, c.seq_len, c.max_seq_len, out=od)
+    callv = lambda: binding.verify(c.pool, qv, c.table, c.seq_len, c.max_seq_len, out=ov)
+    wd = graph_us(calld, torch, check=od)
+    wv = graph_us(callv, torch, check=ov)
+    msd, pd = cold_calls(calld, iters, torch, flush, part=True, binding=binding)
+    msv, pv = cold_calls(callv, iters, torch, flush, part=True, binding=binding)
+    b = sum(c.lengths) * w.kv_bytes_per_token
+    res["head_dim_256"] = {
+        "decode_4x16384": {"warm_us": round(wd, 2), "kv_bytes": b, **cold_record(msd, b, None, pd)},
+        "verify4_4x16384": {"warm_us": round(wv, 2), "kv_bytes": b,
+                            **cold_record(msv, b, attn_flops(c.lengths, 4, w.q_heads, 256), pv)}}
+    cases.append({"name": "head_dim_256_decode", "q": qd, "ks": ks, "vs": vs, "lengths": c.lengths, "window": 0,
+                  "out": od.clone()})
+    cases.append({"name": "head_dim_256_verify4", "q": qv, "ks": ks, "vs": vs, "lengths": c.lengths, "window": 0,
+                  "out": ov.clone()})
 
     # prompt: 2048 tokens in 4 chunks of 512 rows, full layer and sliding layer (window 1024, ring)
     for window in (0, 1024):

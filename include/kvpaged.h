@@ -68,7 +68,7 @@ typedef struct kv_pool_desc {
     int32_t num_pages;       /* > 0 */
     int32_t page_size;       /* P >= 1 positions per page (512 by default; any value works) */
     int32_t num_kv_heads;    /* Hkv >= 1 */
-    int32_t head_dim;        /* D >= 8, a multiple of 8 (attention needs 128 or 512) */
+    int32_t head_dim;        /* D >= 8, a multiple of 8 (attention needs 128, 256 or 512) */
     int32_t max_streams;     /* number of stream ids [0, max_streams) that may lease */
     void *k_pages;           /* device, bf16 [num_pages][Hkv][P][D] */
     void *v_pages;           /* device, bf16 [num_pages][Hkv][P][D] */

@@ -323,7 +323,7 @@ bool call_plan(int D, int G, int R, int S, int Hkv, int P, int max_seq_len, int 
     if (!valu_supported(D, G, nq)) return false;
     // L - base is at most max_seq_len, or the window plus the rows plus the alignment
     int span = max_seq_len;
-    const int align = D == 512 ? 16 : 64;
+    const int align = valu_batch_keys(D);
     if (window > 0 && (int64_t)window + R - 1 + align - 1 < span) span = window + R - 1 + align - 1;
     const ValuPlan vp = valu_plan(D, nq, S, Hkv, span < 1 ? 1 : span);
     p->mp = MfmaPlan{};

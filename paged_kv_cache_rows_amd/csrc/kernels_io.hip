@@ -238,6 +238,8 @@ hipError_t launch_merge(const MergeArgs &a, hipStream_t st) {
         hipLaunchKernelGGL((merge_kernel<128, 128>), dim3(blocks), dim3(64), 0, st, a);
     else if (a.D == 128)
         hipLaunchKernelGGL((merge_kernel<128, 64>), dim3(blocks * 2), dim3(64), 0, st, a);
+    else if (a.D == 256)
+        hipLaunchKernelGGL((merge_kernel<256, 64>), dim3(blocks * 4), dim3(64), 0, st, a);
     else if (a.D == 512)
         hipLaunchKernelGGL((merge_kernel<512, 64>), dim3(blocks * 8), dim3(64), 0, st, a);
     else

@@ -37,7 +37,7 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 template <int D>
 struct MfmaGeom {
     static constexpr int KT = D == 128 ? 64 : 32;       // keys per tile
-    static constexpr int KRS = D + 16;                  // K tile row stride (bf16): 288 or 1056 bytes, so
+    static constexpr int KRS = D + 16;                  // K tile row stride (bf16): 288, 544 or 1056 bytes, so
                                                         // that an MFMA operand read is free of bank conflicts
     static constexpr int CB = D / 8;                    // 16-byte channel blocks per row
     static constexpr int NT = 256;                      // threads
@@ -71,11 +71,11 @@ __device__ __forceinline__ int vt_unit(int ch, int kg) {
     return sr * 32 + ((rr * Geo::UPR + kg) ^ vt_swz(sr));
 }
 
-int mfma_tile_keys(int D) { return D == 512 ? MfmaGeom<512>::KT : MfmaGeom<128>::KT; }
+int mfma_tile_keys(int D) { return D == 512 ? MfmaGeom<512>::KT : D == 256 ? MfmaGeom<256>::KT : MfmaGeom<128>::KT; }
 int mfma_table_mode(int D, int P, int chunk) { return table_mode(P, chunk, mfma_tile_keys(D), 1); }
 
 bool mfma_supported(int D, int G, int R) {
-    return (D == 128 || D == 512) && (G == 4 || G == 8 || G == 12 || G == 16) && R >= 1 && R * G >= 16;
+    return (D == 128 || D == 256 || D == 512) && (G == 4 || G == 8 || G == 12 || G == 16) && R >= 1 && R * G >= 16;
 }
 
 // Query-column blocks per wave, query tiles and chunk length of one call.  Everything here is
@@ -125,6 +125,8 @@ MfmaPlan mfma_plan(int D, int G, int R, int S, int Hkv, int P, int max_seq_len, 
         // took 161 us, in 8 of 4608 (256) 112 us; a 128-row chunk at 40,960 keys takes 144 us in
         // one round against 152 us in two.
         const double us_per_key = 4.0 * D / (0.85 * 8000.0e3 / 256.0), t0 = 5.0;
+        // a d 256 workgroup (34 KB of LDS, two waves per SIMD) shares its CU with another
+        const int64_t per_round = D == 256 ? 512 : 256;
         double best = 0;
         int64_t best_chunk = lo;
         for (int64_t n = 1;; ++n) {
@@ -133,7 +135,7 @@ MfmaPlan mfma_plan(int D, int G, int R, int S, int Hkv, int P, int max_seq_len, 
             if (c <= hi) {
                 int64_t ns = (max_seq_len + c - 1) / c;      // as the call's split count
                 if (window > 0) ns = std::min(ns, (span + c - 1) / c + 1);
-                const int64_t rounds = (groups * ns + 255) / 256;
+                const int64_t rounds = (groups * ns + per_round - 1) / per_round;
                 const double t = (double)rounds * ((double)c * us_per_key + t0);
                 if (best == 0 || t < best) {
                     best = t;
@@ -184,7 +186,7 @@ __global__ __launch_bounds__(256 * KS) void part_mfma_kernel(const PartArgs a) {
     constexpr int NPM = KT / 32;     // 32-key PV k-steps
 
     constexpr int NTH = 256 * KS;    // threads
-    static_assert((KS == 2) == (D == 128) && (KS == 1 || KS == 2), "key sub-tiles: 2 at D = 128, 1 at D = 512");
+    static_assert((KS == 2) == (D == 128) && (KS == 1 || KS == 2), "key sub-tiles: 2 at D = 128, 1 at D = 256 and 512");
 
     // NBUF tile buffers: with two, a step stages the next step's tiles into one buffer while it
     // computes on the other (one barrier per step); one buffer stages and computes in turn
@@ -755,6 +757,10 @@ hipError_t launch_part_mfma(int D, int G, const MfmaPlan &p, const PartArgs &arg
     if (D == 128 && G == 8) return launch_dg<128, 8, 2>(a, st);
     if (D == 128 && G == 12) return launch_dg<128, 12, 2>(a, st);
     if (D == 128 && G == 16) return launch_dg<128, 16, 2>(a, st);
+    if (D == 256 && G == 4) return launch_dg<256, 4, 1>(a, st);
+    if (D == 256 && G == 8) return launch_dg<256, 8, 1>(a, st);
+    if (D == 256 && G == 12) return launch_dg<256, 12, 1>(a, st);
+    if (D == 256 && G == 16) return launch_dg<256, 16, 1>(a, st);
     if (D == 512 && G == 4) return launch_dg<512, 4, 1>(a, st);
     if (D == 512 && G == 8) return launch_dg<512, 8, 1>(a, st);
     if (D == 512 && G == 12) return launch_dg<512, 12, 1>(a, st);

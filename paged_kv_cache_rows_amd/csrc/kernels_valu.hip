@@ -59,7 +59,7 @@ struct ValuGeom {
 ValuPlan valu_plan(int D, int NQ, int S, int Hkv, int span) {
     (void)NQ;
     ValuPlan p;
-    p.align = D == 512 ? ValuGeom<512>::NB : ValuGeom<128>::NB;
+    p.align = valu_batch_keys(D);
     const int64_t groups = (int64_t)S * Hkv;
     int64_t n = (768 + groups - 1) / groups;
     const int64_t piece_keys = 2560 * 128 / D;
@@ -355,12 +355,14 @@ __global__ __launch_bounds__(64 * valu_waves<NQ>()) __attribute__((amdgpu_waves_
                 sc[v] = x;
             }
         }
-        if (QL > 1) {
+        // the QL lanes of a key are lanes kk + NB j: sum their channel segments
+        if constexpr (QL == 4) {
 #pragma unroll
-            for (int v = 0; v < VW; ++v) {
-                sc[v] = sc[v] + __shfl_xor(sc[v], 16);
-                sc[v] = sc[v] + __shfl_xor(sc[v], 32);
-            }
+            for (int v = 0; v < VW; ++v) sc[v] = sc[v] + __shfl_xor(sc[v], 16);
+        }
+        if constexpr (QL >= 2) {
+#pragma unroll
+            for (int v = 0; v < VW; ++v) sc[v] = sc[v] + __shfl_xor(sc[v], 32);
         }
 
         // ---- online softmax (log2 domain).  A batch that every row sees whole needs no mask;
@@ -446,14 +448,18 @@ __global__ __launch_bounds__(64 * valu_waves<NQ>()) __attribute__((amdgpu_waves_
     float l_tot[VW];
 #pragma unroll
     for (int v = 0; v < VW; ++v) l_tot[v] = wave_sum(l_run[v]);
-    if (RPI > 1) {
+    // the RPI lanes of a channel block are lanes lch + LPR j: sum their key rows
+    if constexpr (RPI == 4) {
 #pragma unroll
         for (int v = 0; v < VW; ++v)
 #pragma unroll
-            for (int c = 0; c < 8; ++c) {
-                acc[v][c] = acc[v][c] + __shfl_xor(acc[v][c], 16);
-                if (RPI > 2) acc[v][c] = acc[v][c] + __shfl_xor(acc[v][c], 32);
-            }
+            for (int c = 0; c < 8; ++c) acc[v][c] = acc[v][c] + __shfl_xor(acc[v][c], 16);
+    }
+    if constexpr (RPI >= 2) {
+#pragma unroll
+        for (int v = 0; v < VW; ++v)
+#pragma unroll
+            for (int c = 0; c < 8; ++c) acc[v][c] = acc[v][c] + __shfl_xor(acc[v][c], 32);
     }
 #pragma unroll
     for (int i = 0; i < VW; ++i) {
@@ -468,9 +474,15 @@ __global__ __launch_bounds__(64 * valu_waves<NQ>()) __attribute__((amdgpu_waves_
     }
 }
 
-int valu_batch_keys(int D) { return D == 512 ? ValuGeom<512>::NB : ValuGeom<128>::NB; }
-int valu_rows_per_load(int D) { return D == 512 ? ValuGeom<512>::RPI : ValuGeom<128>::RPI; }
-int valu_table_mode(int D, int P, int chunk) { return D == 512 ? valu_mode<512>(P, chunk) : valu_mode<128>(P, chunk); }
+int valu_batch_keys(int D) {
+    return D == 512 ? ValuGeom<512>::NB : D == 256 ? ValuGeom<256>::NB : ValuGeom<128>::NB;
+}
+int valu_rows_per_load(int D) {
+    return D == 512 ? ValuGeom<512>::RPI : D == 256 ? ValuGeom<256>::RPI : ValuGeom<128>::RPI;
+}
+int valu_table_mode(int D, int P, int chunk) {
+    return D == 512 ? valu_mode<512>(P, chunk) : D == 256 ? valu_mode<256>(P, chunk) : valu_mode<128>(P, chunk);
+}
 template <int NQ>
 static void load_shape(int *waves, int *slots) {
     *waves = valu_waves<NQ>();
@@ -484,7 +496,7 @@ void valu_load_shape(int NQ, int *waves, int *slots_per_wave) {
 }
 
 bool valu_supported(int D, int G, int NQ) {
-    if (D != 128 && D != 512) return false;
+    if (D != 128 && D != 256 && D != 512) return false;
     if (G == 4) return NQ == 4 || NQ == 8 || NQ == 12;
     if (G == 8) return NQ == 8;
     if (G == 12) return NQ == 12;
@@ -509,6 +521,8 @@ hipError_t launch_part_valu(int D, int G, int NQ, const PartArgs &a, int S, hipS
     if (D == d && G == g && NQ == nq) return launch_one<d, g, nq>(a, S, st);
     KVP_VALU_CASE(128, 4, 4) KVP_VALU_CASE(128, 4, 8) KVP_VALU_CASE(128, 4, 12) KVP_VALU_CASE(128, 8, 8)
     KVP_VALU_CASE(128, 12, 12)
+    KVP_VALU_CASE(256, 4, 4) KVP_VALU_CASE(256, 4, 8) KVP_VALU_CASE(256, 4, 12) KVP_VALU_CASE(256, 8, 8)
+    KVP_VALU_CASE(256, 12, 12)
     KVP_VALU_CASE(512, 4, 4) KVP_VALU_CASE(512, 4, 8) KVP_VALU_CASE(512, 4, 12) KVP_VALU_CASE(512, 8, 8)
     KVP_VALU_CASE(512, 12, 12)
 #undef KVP_VALU_CASE

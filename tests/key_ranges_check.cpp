@@ -351,7 +351,7 @@ int main(int argc, char **argv) {
         if (!std::strcmp(argv[i], "--plant")) plant = argv[i + 1];
     std::mt19937 rng(20240611u);
     std::vector<Shape> shapes;
-    const int Ds[] = {128, 512};
+    const int Ds[] = {128, 256, 512};
     // (G, R) pairs of the VALU kernel (R G < 16) and of the MFMA kernel
     const int GR[][2] = {{4, 1}, {4, 2}, {4, 3}, {8, 1}, {12, 1}, {4, 4}, {4, 8}, {8, 2}, {8, 4},
                          {8, 8}, {8, 32}, {12, 2}, {12, 4}, {16, 1}, {16, 4}, {4, 128}, {8, 256}};
