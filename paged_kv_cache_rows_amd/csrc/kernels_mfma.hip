@@ -190,7 +190,7 @@ __global__ __launch_bounds__(256 * KS) void part_mfma_kernel(const PartArgs a) {
 
     // NBUF tile buffers: with two, a step stages the next step's tiles into one buffer while it
     // computes on the other (one barrier per step); one buffer stages and computes in turn
-    constexpr int NBUF = KS == 2 ? 2 : 1;
+    constexpr int NBUF = (KS == 2 || (D == 256 && MODE == 0)) ? 2 : 1;
     __shared__ __attribute__((aligned(16))) uint16_t k_lds_all[NBUF][KS][KT * KRS];
     __shared__ __attribute__((aligned(16))) uint2 vt_lds_all[NBUF][KS][D * KT / 4];
     __shared__ int32_t t_lds[TC];
@@ -609,6 +609,10 @@ __global__ __launch_bounds__(256 * KS) void part_mfma_kernel(const PartArgs a) {
         lds_fence();
         f32x4_t s0[QW][NB], s1[QW][NB];
         qk(0, 0, s0);
+        // the first iteration stages K(2) into K buffer 0, which qk(0) has just read: every
+        // wave must be done with it first (later iterations write a buffer only after a barrier
+        // that follows its last read)
+        lds_fence();
         // Steps it and it + 1 per iteration.  The last iterations (the second loop, the same
         // body) neither load nor stage steps past the split, so that the split ends when its
         // own data has arrived, not after loads that would only reread its last tile (4-stream
@@ -738,7 +742,7 @@ static hipError_t launch_dgq(const PartArgs &a, hipStream_t st) {
 
 template <int D, int G, int KS>
 static hipError_t launch_dg(const PartArgs &a, hipStream_t st) {
-    if constexpr (D == 128)
+    if constexpr (D == 128 || D == 256)
         if (a.tiles == 1) return launch_dgq<D, G, 1, KS, true>(a, st);
     return launch_dgq<D, G, 1, KS, false>(a, st);
 }
