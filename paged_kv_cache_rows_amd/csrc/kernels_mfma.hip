@@ -13,7 +13,9 @@
 //    transposed into 8-byte units of 4 keys of one channel.  Each thread loads 4 (or 8)
 //    consecutive keys of one 8-channel block, so the transpose is a register permute and the
 //    unit stores are 8 bytes wide; the units are XOR-swizzled so that both the stores and the
-//    MFMA operand reads touch every LDS bank equally.
+//    MFMA operand reads touch every LDS bank equally.  At d 128 with pages holding whole tiles
+//    the tiles go from memory straight into LDS instead (DMA below), and V^T is read from plain
+//    rows with transposing LDS reads.
 //  * Scores are computed transposed, S^T = K Q^T, with v_mfma_f32_16x16x32_bf16: the wave's
 //    queries are the B operand, held in registers for the whole chunk, and each K fragment read
 //    from LDS feeds QW MFMAs.  In the C layout a lane owns one query column and 4 keys per
@@ -33,6 +35,8 @@ namespace kvp {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+#define LDS __attribute__((address_space(3)))
 
 template <int D>
 struct MfmaGeom {
@@ -161,6 +165,22 @@ MfmaPlan mfma_plan(int D, int G, int R, int S, int Hkv, int P, int max_seq_len, 
     return p;
 }
 
+// Waits for all of this wave's vector memory operations (vmcnt 0; expcnt and lgkmcnt left
+// alone): loads that write LDS directly have landed once it returns.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// 16 bytes per lane from global memory straight into LDS: lane l's bytes land at dst + 16 l
+// (dst wave-uniform).  NT: nontemporal.
+template <bool NT>
+__device__ __forceinline__ void load_to_lds(const char *src, char *dst) {
+    __builtin_amdgcn_global_load_lds((const void *)src, (LDS void *)dst, 16, 0, NT ? 2 : 0);
+}
+
+// Transposed 8-byte LDS read of 16-bit elements (ds_read_b64_tr_b16; see the DMA layout).
+__device__ __forceinline__ v4i16_t lds_read_tr16(const char *p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS v4i16_t *)(p));
+}
+
 __device__ __forceinline__ f32x4_t mfma16(const bf16x8_t &a, const bf16x8_t &b, const f32x4_t &c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
@@ -175,10 +195,21 @@ __device__ __forceinline__ f32x4_t mfma16(const bf16x8_t &a, const bf16x8_t &b, 
 // compute sub-tile g of each 2 KT-key step with an online softmax of their own, and the two
 // states are combined through LDS at the end, which halves the tile chain of a workgroup
 // without splitting the keys over workgroups (no partials in memory).
-template <int D, int G, int QW, int MODE, int KS, bool NTL>
+// DMA (d 128, pages holding whole tiles): K and V go from memory straight into LDS
+// (global_load_lds_dwordx4: lane l of a load writes the 16 bytes at the load's LDS base + 16 l,
+// from an address of its own), with no pass through registers and no staging instructions.  A
+// tile is kept as plain rows of 256 bytes whose 16-byte pieces are permuted per row (an XOR
+// with the row number, chosen through each lane's source address), and the V^T operand of PV
+// comes from transposed 8-byte LDS reads (ds_read_b64_tr_b16): within each 16-lane group,
+// lane 4 a + e receives element e of the 8-byte pieces that lanes a, a + 4, a + 8 and a + 12
+// address, i.e. four consecutive keys of one channel when those lanes address four
+// consecutive rows.
+template <int D, int G, int QW, int MODE, int KS, bool NTL, bool DMA>
 __global__ __launch_bounds__(256 * KS) void part_mfma_kernel(const PartArgs a) {
     using Geo = MfmaGeom<D>;
     constexpr int KT = Geo::KT, KRS = Geo::KRS, CB = Geo::CB, KPT = Geo::KPT, TC = Geo::TC;
+    static_assert(!DMA || (D == 128 && MODE == 0 && KS == 2), "direct-to-LDS tiles: d 128, whole tiles per page");
+    constexpr int KROW = DMA ? D : KRS;   // K tile row stride (bf16)
     constexpr int M = 64 * QW;       // query vectors per workgroup
     constexpr int NB = KT / 16;      // 16-key blocks per tile
     constexpr int NKB = D / 32;      // 32-channel blocks (QK k-steps)
@@ -191,7 +222,8 @@ __global__ __launch_bounds__(256 * KS) void part_mfma_kernel(const PartArgs a) {
     // NBUF tile buffers: with two, a step stages the next step's tiles into one buffer while it
     // computes on the other (one barrier per step); one buffer stages and computes in turn
     constexpr int NBUF = (KS == 2 || (D == 256 && MODE == 0)) ? 2 : 1;
-    __shared__ __attribute__((aligned(16))) uint16_t k_lds_all[NBUF][KS][KT * KRS];
+    __shared__ __attribute__((aligned(16))) uint16_t k_lds_all[NBUF][KS][KT * KROW];
+    // V^T units, or with DMA the V rows of a tile (KT x D bf16, the same bytes)
     __shared__ __attribute__((aligned(16))) uint2 vt_lds_all[NBUF][KS][D * KT / 4];
     __shared__ int32_t t_lds[TC];
 
@@ -323,7 +355,7 @@ __global__ __launch_bounds__(256 * KS) void part_mfma_kernel(const PartArgs a) {
     const int kc = (tid & 255) % CB, kq = (tid & 255) / CB;
     // buffer `buf` of the sub-tile this thread stages (ksub: thread tid stages sub-tile tid / 256,
     // which is also the sub-tile its wave computes)
-    constexpr int KBUF = KS * KT * KRS, VBUF = KS * D * KT / 4;
+    constexpr int KBUF = KS * KT * KROW, VBUF = KS * D * KT / 4;
     uint16_t *const k_st0 = k_lds_all[0][ksub];
     uint2 *const vt_st0 = vt_lds_all[0][ksub];
     u32x4 kreg0[KPT], vreg0[KPT], kreg1[KPT], vreg1[KPT];
@@ -391,11 +423,32 @@ __global__ __launch_bounds__(256 * KS) void part_mfma_kernel(const PartArgs a) {
 #pragma unroll
     for (int c = 0; c < 8; ++c) pv_off[c] = 16 * (8 * col + ((grp ^ (col >> 1)) ^ c));
     const bf16x8_t ones8 = __builtin_bit_cast(bf16x8_t, u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
+    // DMA: this lane's byte offsets in a tile of 256-byte rows.
+    //  - sources of its 16-byte pieces: rows 16 wave + 4 j + (lane >> 4) of its group's sub-tile;
+    //    LDS piece (lane & 15) of a row holds the row's piece (lane & 15) ^ f(row), f = row & 15
+    //    for K and 2 (row & 7) for V (so that V's 32-byte halves of 16 channels stay whole)
+    //  - K operand reads: row 16 nb + col, piece 4 kb + grp, which sits at piece (4 kb + grp) ^ col
+    //  - V^T operand reads: row 4 grp + (col >> 2) (+ 32 pm + 16 hh), channels 16 cb + 4 (col & 3)
+    int k_src[4], v_src[4], k_rd[NKB], v_rd[NCB];
+    if constexpr (DMA) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int r = 16 * wave + 4 * j + (lane >> 4);
+            k_src[j] = r * 2 * D + 16 * ((lane & 15) ^ (r & 15));
+            v_src[j] = r * 2 * D + 16 * ((lane & 15) ^ (2 * (r & 7)));
+        }
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) k_rd[kb] = col * 2 * D + 16 * ((4 * kb + grp) ^ col);
+        const int vr = 4 * grp + (col >> 2);
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) v_rd[cb] = vr * 2 * D + 32 * (cb ^ (vr & 7)) + 8 * (col & 3);
+    }
 
     // Step it covers sub-tiles KS it .. KS it + KS - 1; loads past the last sub-tile reread it
     // (in bounds, never computed on), and sub-tiles past it are all masked out.
     const int kt_last = kt_first + (nt - 1) * KT;
     const int nsteps = (nt + KS - 1) / KS;
+    auto ts_of = [&](int it) { return kt_first + (it * KS + ksub) * KT; };
     // stage step it's sub-tile of this thread from (kreg, vreg) into buffer buf
     // stage K rows as loaded into buffer buf
     auto stage_k = [&](const u32x4 (&kreg)[KPT], int buf) {
@@ -407,7 +460,7 @@ __global__ __launch_bounds__(256 * KS) void part_mfma_kernel(const PartArgs a) {
     // stage V of step it transposed into 4-key units of buffer buf, keys outside [kbeg, kend)
     // zeroed (they may be unused slots holding NaN)
     auto stage_v = [&](int it, const u32x4 (&vreg)[KPT], int buf) {
-        const int ts = kt_first + (it * KS + ksub) * KT;          // sub-tile this thread stages
+        const int ts = ts_of(it);                                 // sub-tile this thread stages
         uint2 *const vt_st = vt_st0 + buf * VBUF;
         const bool inside = ts >= kbeg && ts + KT <= kend;
 #pragma unroll
@@ -445,12 +498,57 @@ __global__ __launch_bounds__(256 * KS) void part_mfma_kernel(const PartArgs a) {
         stage_k(kreg, buf);
         stage_v(it, vreg, buf);
     };
-    auto ts_of = [&](int it) { return kt_first + (it * KS + ksub) * KT; };
+    // DMA: the loads of a step, issued together at its start: the page of this thread's group's
+    // sub-tile of each operand (null past the split), then 4 loads of 1 KB (4 rows) per wave and
+    // operand.  (Spreading the loads over the step's MFMAs measured slower.)
+    struct Pend {
+        const char *k, *v;   // sources of this wave's rows of K and V
+        char *kd, *vd;       // their LDS rows
+    };
+    auto plan_one = [&](int it, const uint16_t *pages) -> const char * {
+        const int ts = ts_of(it);
+        if (ts >= kend) return nullptr;
+        const int idx = (int)((unsigned)ts / (unsigned)P);
+        const int pg = __builtin_amdgcn_readfirstlane(cached_page<TC>(t_lds, idx - idx0));
+        return reinterpret_cast<const char *>(pages + (size_t)pg * page_elems + head_off + (size_t)(ts - idx * P) * D);
+    };
+    auto plan = [&](int itk, char *kbuf, int itv, char *vbuf) {
+        Pend pd;
+        pd.k = plan_one(itk, a.k_pages);
+        pd.v = plan_one(itv, a.v_pages);
+        pd.kd = kbuf + wave * 16 * 2 * D;
+        pd.vd = vbuf + wave * 16 * 2 * D;
+        return pd;
+    };
+    auto issue = [&](const Pend &pd) {
+        if constexpr (DMA) {
+            if (pd.k) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) load_to_lds<NTL>(pd.k + k_src[j], pd.kd + j * 4 * 2 * D);
+            }
+            if (pd.v) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) load_to_lds<NTL>(pd.v + v_src[j], pd.vd + j * 4 * 2 * D);
+            }
+        }
+    };
+    // DMA: once this wave's loads of V for step it have landed, zero its rows of keys outside
+    // [kbeg, kend) (unused slots may hold NaN, which a zero weight would not cancel)
+    auto fix_v = [&](int it, int buf) {
+        const int ts = ts_of(it);
+        if (ts >= kend || (ts >= kbeg && ts + KT <= kend)) return;
+        char *const dst = reinterpret_cast<char *>(vt_st0 + buf * VBUF) + wave * 16 * 2 * D + 16 * lane;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int key = ts + 16 * wave + 4 * j + (lane >> 4);
+            if (key < kbeg || key >= kend) *reinterpret_cast<u32x4 *>(dst + j * 4 * 2 * D) = u32x4{0u, 0u, 0u, 0u};
+        }
+    };
     // compute step it's sub-tile of this wave from buffer buf
     // S^T of step it's sub-tile for this wave's query columns, from K buffer buf; each K
     // fragment feeds QW MFMAs (a padded step past the split computes nothing)
     auto qk = [&](int it, int buf, f32x4_t (&sacc)[QW][NB]) {
-        const int tb = kt_first + (it * KS + ksub) * KT;          // sub-tile this wave computes
+        const int tb = ts_of(it);                                 // sub-tile this wave computes
         if (tb >= kend || !wave_live) return;
         const uint16_t *const k_lds = k_st0 + buf * KBUF;
 #pragma unroll
@@ -459,7 +557,11 @@ __global__ __launch_bounds__(256 * KS) void part_mfma_kernel(const PartArgs a) {
             for (int b = 0; b < QW; ++b) sacc[b][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb) {
-                const bf16x8_t kf = *reinterpret_cast<const bf16x8_t *>(k_lds + (16 * nb + col) * KRS + 32 * kb + 8 * grp);
+                bf16x8_t kf;
+                if constexpr (DMA)
+                    kf = *reinterpret_cast<const bf16x8_t *>(reinterpret_cast<const char *>(k_lds) + k_rd[kb] + 4096 * nb);
+                else
+                    kf = *reinterpret_cast<const bf16x8_t *>(k_lds + (16 * nb + col) * KRS + 32 * kb + 8 * grp);
 #pragma unroll
                 for (int b = 0; b < QW; ++b) sacc[b][nb] = mfma16(kf, qf[b][kb], sacc[b][nb]);
             }
@@ -468,7 +570,7 @@ __global__ __launch_bounds__(256 * KS) void part_mfma_kernel(const PartArgs a) {
     // mask, online softmax and O^T += V^T P^T of step it's sub-tile, from its scores and V
     // buffer buf
     auto smpv = [&](int it, int buf, f32x4_t (&sacc)[QW][NB]) {
-        const int tb = kt_first + (it * KS + ksub) * KT;
+        const int tb = ts_of(it);
         if (tb >= kend || !wave_live) return;
         const uint2 *const vt_lds = vt_st0 + buf * VBUF;
         const bool full = tb >= kbeg && tb + KT <= kend && tb + KT - 1 <= hi_full && tb >= lo_full;
@@ -535,7 +637,23 @@ __global__ __launch_bounds__(256 * KS) void part_mfma_kernel(const PartArgs a) {
         // and 32 pm + 16 + 4 grp + {0..3}; each V fragment feeds QW MFMAs
         // (kept opaque so that the 2 NCB NPM addresses are formed in the loop, one ALU op
         // each, not held in registers across it)
-        if constexpr (D == 128) {
+        if constexpr (DMA) {
+            // rows 32 pm + 4 grp + {0..3} and 32 pm + 16 + 4 grp + {0..3} of channel 16 cb + col,
+            // two transposed reads per operand
+            const char *vb = reinterpret_cast<const char *>(vt_lds);
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb) {
+#pragma unroll
+                for (int pm = 0; pm < NPM; ++pm) {
+                    const v4i16_t lo = lds_read_tr16(vb + v_rd[cb] + 256 * (32 * pm));
+                    const v4i16_t hi = lds_read_tr16(vb + v_rd[cb] + 256 * (32 * pm + 16));
+                    const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
+                    const bf16x8_t vv = __builtin_bit_cast(bf16x8_t, u32x4{l2.x, l2.y, h2.x, h2.y});
+#pragma unroll
+                    for (int b = 0; b < QW; ++b) o[b][cb] = mfma16(vv, pf[b][pm], o[b][cb]);
+                }
+            }
+        } else if constexpr (D == 128) {
             // unit vt_pair(16 cb + col, 4 pm + grp) = 8 (16 cb + col) + ((grp ^ (col >> 1)) ^ (4 pm ^ cb)):
             // the lane's offset for the constant (4 pm) ^ cb, plus 2048 bytes per channel block
             const char *vtb = reinterpret_cast<const char *>(vt_lds);
@@ -580,7 +698,36 @@ __global__ __launch_bounds__(256 * KS) void part_mfma_kernel(const PartArgs a) {
         lds_fence();
         compute(it, 0);
     };
-    if constexpr (NBUF == 2) {
+    if constexpr (DMA) {
+        // The same pipeline with the loads going straight to LDS: step it computes the scores
+        // of step it + 1 and the softmax and PV of step it, while K of step it + 2 and V of step
+        // it + 1 load into the buffers whose last readers finished before the previous barrier;
+        // each step ends by waiting for its loads, then the barrier.
+        char *const kb0 = reinterpret_cast<char *>(k_st0), *const kb1 = reinterpret_cast<char *>(k_st0 + KBUF);
+        char *const vb0 = reinterpret_cast<char *>(vt_st0), *const vb1 = reinterpret_cast<char *>(vt_st0 + VBUF);
+        issue(plan(0, kb0, 0, vb0));          // K(0), V(0)
+        issue(plan(1, kb1, nsteps, vb1));     // K(1)
+        wait_vmem();
+        fix_v(0, 0);
+        lds_fence();
+        f32x4_t s0[QW][NB], s1[QW][NB];
+        qk(0, 0, s0);
+        lds_fence();   // K buffer 0 is loaded again next
+        for (int it = 0; it < nsteps; it += 2) {
+            issue(plan(it + 2, kb0, it + 1, vb1));
+            qk(it + 1, 1, s1);
+            smpv(it, 0, s0);
+            wait_vmem();
+            fix_v(it + 1, 1);
+            lds_fence();
+            issue(plan(it + 3, kb1, it + 2, vb0));
+            qk(it + 2, 0, s0);
+            smpv(it + 1, 1, s1);
+            wait_vmem();
+            fix_v(it + 2, 0);
+            lds_fence();
+        }
+    } else if constexpr (NBUF == 2) {
         // Software pipeline over two K and two V buffers.  Step it computes the scores of step
         // it + 1 (MFMA) before the softmax and PV of step it, whose scores came from the step
         // before: the MFMAs and the softmax of one wave are independent and overlap.  K is
@@ -670,7 +817,7 @@ __global__ __launch_bounds__(256 * KS) void part_mfma_kernel(const PartArgs a) {
         // through LDS (field f of lane (wave, lane) at f * 256 + 64 wave + lane), then only
         // waves 0..3 go on
         constexpr int NF = 4 * NCB + 2;
-        static_assert(NF * 256 * 4 <= KS * KT * KRS * 2, "exchange fits the K tiles");
+        static_assert(NF * 256 * 4 <= NBUF * KS * KT * KROW * 2, "exchange fits the K tiles");
         float *xch = reinterpret_cast<float *>(&k_lds_all[0][0][0]);
         const int xi = 64 * wave + lane;
         lds_fence();
@@ -733,9 +880,15 @@ static hipError_t launch_dgq(const PartArgs &a, hipStream_t st) {
     using Geo = MfmaGeom<D>;
     const dim3 grid(8 * a.per_xcd);
     switch (table_mode(a.P, a.chunk, Geo::KT, 1)) {
-        case 0: hipLaunchKernelGGL((part_mfma_kernel<D, G, QW, 0, KS, NTL>), grid, dim3(256 * KS), 0, st, a); break;
-        case 1: hipLaunchKernelGGL((part_mfma_kernel<D, G, QW, 1, KS, NTL>), grid, dim3(256 * KS), 0, st, a); break;
-        default: hipLaunchKernelGGL((part_mfma_kernel<D, G, QW, 2, KS, NTL>), grid, dim3(256 * KS), 0, st, a); break;
+        case 0:
+            // at d 128, pages holding whole tiles: loads straight into LDS
+            if constexpr (D == 128)
+                hipLaunchKernelGGL((part_mfma_kernel<D, G, QW, 0, KS, NTL, true>), grid, dim3(256 * KS), 0, st, a);
+            else
+                hipLaunchKernelGGL((part_mfma_kernel<D, G, QW, 0, KS, NTL, false>), grid, dim3(256 * KS), 0, st, a);
+            break;
+        case 1: hipLaunchKernelGGL((part_mfma_kernel<D, G, QW, 1, KS, NTL, false>), grid, dim3(256 * KS), 0, st, a); break;
+        default: hipLaunchKernelGGL((part_mfma_kernel<D, G, QW, 2, KS, NTL, false>), grid, dim3(256 * KS), 0, st, a); break;
     }
     return hipGetLastError();
 }
