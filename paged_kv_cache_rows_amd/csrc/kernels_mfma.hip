@@ -203,9 +203,11 @@ __device__ __forceinline__ f32x4_t mfma16(const bf16x8_t &a, const bf16x8_t &b, 
 // comes from transposed 8-byte LDS reads (ds_read_b64_tr_b16): within each 16-lane group,
 // lane 4 a + e receives element e of the 8-byte pieces that lanes a, a + 4, a + 8 and a + 12
 // address, i.e. four consecutive keys of one channel when those lanes address four
-// consecutive rows.
+// consecutive rows.  Two more waves (a workgroup of 640 threads) issue all the loads: a CU's
+// vector memory path takes about 18 cycles per 1 KB load, so a burst of a step's 64 loads
+// would otherwise hold the computing waves at issue.
 template <int D, int G, int QW, int MODE, int KS, bool NTL, bool DMA>
-__global__ __launch_bounds__(256 * KS) void part_mfma_kernel(const PartArgs a) {
+__global__ __launch_bounds__(DMA ? 640 : 256 * KS) void part_mfma_kernel(const PartArgs a) {
     using Geo = MfmaGeom<D>;
     constexpr int KT = Geo::KT, KRS = Geo::KRS, CB = Geo::CB, KPT = Geo::KPT, TC = Geo::TC;
     static_assert(!DMA || (D == 128 && MODE == 0 && KS == 2), "direct-to-LDS tiles: d 128, whole tiles per page");
@@ -216,7 +218,7 @@ __global__ __launch_bounds__(256 * KS) void part_mfma_kernel(const PartArgs a) {
     constexpr int NCB = D / 16;      // 16-channel blocks (PV output blocks)
     constexpr int NPM = KT / 32;     // 32-key PV k-steps
 
-    constexpr int NTH = 256 * KS;    // threads
+    constexpr int NTH = DMA ? 640 : 256 * KS;    // threads (with DMA: 8 computing waves and 2 loading)
     static_assert((KS == 2) == (D == 128) && (KS == 1 || KS == 2), "key sub-tiles: 2 at D = 128, 1 at D = 256 and 512");
 
     // NBUF tile buffers: with two, a step stages the next step's tiles into one buffer while it
@@ -232,7 +234,12 @@ __global__ __launch_bounds__(256 * KS) void part_mfma_kernel(const PartArgs a) {
     // wave-uniform by construction; readfirstlane tells the compiler, so that tests on them
     // (a sub-tile inside the split, a full tile) become scalar branches, not exec-mask ones
     const int wave = __builtin_amdgcn_readfirstlane((tid >> 6) & 3);   // column wave: query vectors 16 (wave QW + b) + col
-    const int ksub = __builtin_amdgcn_readfirstlane(tid >> 8);         // key sub-tile this wave computes (and thread stages)
+    const int ksub = __builtin_amdgcn_readfirstlane(min(tid >> 8, KS - 1));   // key sub-tile this wave computes (and thread stages)
+    // DMA: waves 8 and 9 only load (wave 8 + p the sub-tiles p of every step), so that the
+    // computing waves never wait at the issue of a burst of loads while the CU's vector memory
+    // path drains it
+    const bool producer = DMA && tid >= 512;
+    const int psub = __builtin_amdgcn_readfirstlane(producer ? (tid >> 6) - 8 : 0);
     const int col = lane & 15, grp = lane >> 4;
     // work item: the dispatcher hands workgroups to the 8 XCDs round-robin (dispatch id
     // d goes to XCD d mod 8), so XCD x gets the contiguous items [x per, (x + 1) per), ordered
@@ -423,20 +430,13 @@ __global__ __launch_bounds__(256 * KS) void part_mfma_kernel(const PartArgs a) {
 #pragma unroll
     for (int c = 0; c < 8; ++c) pv_off[c] = 16 * (8 * col + ((grp ^ (col >> 1)) ^ c));
     const bf16x8_t ones8 = __builtin_bit_cast(bf16x8_t, u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
-    // DMA: this lane's byte offsets in a tile of 256-byte rows.
-    //  - sources of its 16-byte pieces: rows 16 wave + 4 j + (lane >> 4) of its group's sub-tile;
-    //    LDS piece (lane & 15) of a row holds the row's piece (lane & 15) ^ f(row), f = row & 15
-    //    for K and 2 (row & 7) for V (so that V's 32-byte halves of 16 channels stay whole)
-    //  - K operand reads: row 16 nb + col, piece 4 kb + grp, which sits at piece (4 kb + grp) ^ col
-    //  - V^T operand reads: row 4 grp + (col >> 2) (+ 32 pm + 16 hh), channels 16 cb + 4 (col & 3)
-    int k_src[4], v_src[4], k_rd[NKB], v_rd[NCB];
+    // DMA: a tile is kept as 256-byte rows; LDS piece p of row r holds the row's 16-byte piece
+    // p ^ f(r), f = r & 15 for K and 2 (r & 7) for V (V's 32-byte halves of 16 channels stay
+    // whole).  This lane's byte offsets of its operand reads:
+    //  - K: row 16 nb + col, piece 4 kb + grp, which sits at piece (4 kb + grp) ^ col;
+    //  - V^T: row 4 grp + (col >> 2) (+ 32 pm + 16 hh), channels 16 cb + 4 (col & 3).
+    int k_rd[NKB], v_rd[NCB];
     if constexpr (DMA) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int r = 16 * wave + 4 * j + (lane >> 4);
-            k_src[j] = r * 2 * D + 16 * ((lane & 15) ^ (r & 15));
-            v_src[j] = r * 2 * D + 16 * ((lane & 15) ^ (2 * (r & 7)));
-        }
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) k_rd[kb] = col * 2 * D + 16 * ((4 * kb + grp) ^ col);
         const int vr = 4 * grp + (col >> 2);
@@ -497,52 +497,6 @@ __global__ __launch_bounds__(256 * KS) void part_mfma_kernel(const PartArgs a) {
     auto stage = [&](int it, const u32x4 (&kreg)[KPT], const u32x4 (&vreg)[KPT], int buf) {
         stage_k(kreg, buf);
         stage_v(it, vreg, buf);
-    };
-    // DMA: the loads of a step, issued together at its start: the page of this thread's group's
-    // sub-tile of each operand (null past the split), then 4 loads of 1 KB (4 rows) per wave and
-    // operand.  (Spreading the loads over the step's MFMAs measured slower.)
-    struct Pend {
-        const char *k, *v;   // sources of this wave's rows of K and V
-        char *kd, *vd;       // their LDS rows
-    };
-    auto plan_one = [&](int it, const uint16_t *pages) -> const char * {
-        const int ts = ts_of(it);
-        if (ts >= kend) return nullptr;
-        const int idx = (int)((unsigned)ts / (unsigned)P);
-        const int pg = __builtin_amdgcn_readfirstlane(cached_page<TC>(t_lds, idx - idx0));
-        return reinterpret_cast<const char *>(pages + (size_t)pg * page_elems + head_off + (size_t)(ts - idx * P) * D);
-    };
-    auto plan = [&](int itk, char *kbuf, int itv, char *vbuf) {
-        Pend pd;
-        pd.k = plan_one(itk, a.k_pages);
-        pd.v = plan_one(itv, a.v_pages);
-        pd.kd = kbuf + wave * 16 * 2 * D;
-        pd.vd = vbuf + wave * 16 * 2 * D;
-        return pd;
-    };
-    auto issue = [&](const Pend &pd) {
-        if constexpr (DMA) {
-            if (pd.k) {
-#pragma unroll
-                for (int j = 0; j < 4; ++j) load_to_lds<NTL>(pd.k + k_src[j], pd.kd + j * 4 * 2 * D);
-            }
-            if (pd.v) {
-#pragma unroll
-                for (int j = 0; j < 4; ++j) load_to_lds<NTL>(pd.v + v_src[j], pd.vd + j * 4 * 2 * D);
-            }
-        }
-    };
-    // DMA: once this wave's loads of V for step it have landed, zero its rows of keys outside
-    // [kbeg, kend) (unused slots may hold NaN, which a zero weight would not cancel)
-    auto fix_v = [&](int it, int buf) {
-        const int ts = ts_of(it);
-        if (ts >= kend || (ts >= kbeg && ts + KT <= kend)) return;
-        char *const dst = reinterpret_cast<char *>(vt_st0 + buf * VBUF) + wave * 16 * 2 * D + 16 * lane;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int key = ts + 16 * wave + 4 * j + (lane >> 4);
-            if (key < kbeg || key >= kend) *reinterpret_cast<u32x4 *>(dst + j * 4 * 2 * D) = u32x4{0u, 0u, 0u, 0u};
-        }
     };
     // compute step it's sub-tile of this wave from buffer buf
     // S^T of step it's sub-tile for this wave's query columns, from K buffer buf; each K
@@ -700,31 +654,76 @@ __global__ __launch_bounds__(256 * KS) void part_mfma_kernel(const PartArgs a) {
     };
     if constexpr (DMA) {
         // The same pipeline with the loads going straight to LDS: step it computes the scores
-        // of step it + 1 and the softmax and PV of step it, while K of step it + 2 and V of step
-        // it + 1 load into the buffers whose last readers finished before the previous barrier;
-        // each step ends by waiting for its loads, then the barrier.
-        char *const kb0 = reinterpret_cast<char *>(k_st0), *const kb1 = reinterpret_cast<char *>(k_st0 + KBUF);
-        char *const vb0 = reinterpret_cast<char *>(vt_st0), *const vb1 = reinterpret_cast<char *>(vt_st0 + VBUF);
-        issue(plan(0, kb0, 0, vb0));          // K(0), V(0)
-        issue(plan(1, kb1, nsteps, vb1));     // K(1)
-        wait_vmem();
-        fix_v(0, 0);
-        lds_fence();
+        // of step it + 1 and the softmax and PV of step it, while the loading waves bring K of
+        // step it + 2 and V of step it + 1 into the buffers whose last readers finished before
+        // the previous barrier; they wait for their loads before each barrier.  (With every
+        // wave issuing its share of a step's loads at the step's start, the 2,048-token prompt
+        // took 111.5 µs against 99.5 µs now; spreading those loads over the step's MFMAs took
+        // 117.5 µs.)
+        if (producer) {
+            // loads of sub-tile psub of step it of one operand into LDS rows at sub (16 loads of
+            // 4 rows, the pieces permuted through each lane's source address); V rows of keys
+            // outside [kbeg, kend) are zeroed once they have landed (unused slots may hold NaN,
+            // which a zero weight would not cancel)
+            char *const pk0 = reinterpret_cast<char *>(k_lds_all[0][psub]), *const pk1 = reinterpret_cast<char *>(k_lds_all[1][psub]);
+            char *const pv0 = reinterpret_cast<char *>(vt_lds_all[0][psub]), *const pv1 = reinterpret_cast<char *>(vt_lds_all[1][psub]);
+            auto pload = [&](int it, const uint16_t *pages, char *sub, bool is_v) {
+                const int ts = kt_first + (it * KS + psub) * KT;
+                if (ts >= kend) return;
+                const int idx = (int)((unsigned)ts / (unsigned)P);
+                const int pg = __builtin_amdgcn_readfirstlane(cached_page<TC>(t_lds, idx - idx0));
+                const char *base = reinterpret_cast<const char *>(pages + (size_t)pg * page_elems + head_off +
+                                                                  (size_t)(ts - idx * P) * D);
+#pragma unroll
+                for (int j = 0; j < KT / 4; ++j) {
+                    const int r = 4 * j + (lane >> 4);
+                    const int piece = (lane & 15) ^ (is_v ? 2 * (r & 7) : (r & 15));
+                    load_to_lds<NTL>(base + r * 2 * D + 16 * piece, sub + j * 4 * 2 * D);
+                }
+            };
+            auto pfix = [&](int it, char *sub) {
+                const int ts = kt_first + (it * KS + psub) * KT;
+                if (ts >= kend || (ts >= kbeg && ts + KT <= kend)) return;
+#pragma unroll
+                for (int j = 0; j < KT / 4; ++j) {
+                    const int key = ts + 4 * j + (lane >> 4);
+                    if (key < kbeg || key >= kend)
+                        *reinterpret_cast<u32x4 *>(sub + j * 4 * 2 * D + 16 * lane) = u32x4{0u, 0u, 0u, 0u};
+                }
+            };
+            pload(0, a.k_pages, pk0, false);
+            pload(1, a.k_pages, pk1, false);
+            pload(0, a.v_pages, pv0, true);
+            wait_vmem();
+            pfix(0, pv0);
+            lds_fence();
+            lds_fence();   // the computing waves' scores of step 0
+            for (int it = 0; it < nsteps; it += 2) {
+                pload(it + 2, a.k_pages, pk0, false);
+                pload(it + 1, a.v_pages, pv1, true);
+                wait_vmem();
+                pfix(it + 1, pv1);
+                lds_fence();
+                pload(it + 3, a.k_pages, pk1, false);
+                pload(it + 2, a.v_pages, pv0, true);
+                wait_vmem();
+                pfix(it + 2, pv0);
+                lds_fence();
+            }
+            lds_fence();   // the two barriers of the key groups' combine
+            lds_fence();
+            return;
+        }
+        lds_fence();   // step 0's tiles have landed
         f32x4_t s0[QW][NB], s1[QW][NB];
         qk(0, 0, s0);
         lds_fence();   // K buffer 0 is loaded again next
         for (int it = 0; it < nsteps; it += 2) {
-            issue(plan(it + 2, kb0, it + 1, vb1));
             qk(it + 1, 1, s1);
             smpv(it, 0, s0);
-            wait_vmem();
-            fix_v(it + 1, 1);
             lds_fence();
-            issue(plan(it + 3, kb1, it + 2, vb0));
             qk(it + 2, 0, s0);
             smpv(it + 1, 1, s1);
-            wait_vmem();
-            fix_v(it + 2, 0);
             lds_fence();
         }
     } else if constexpr (NBUF == 2) {
@@ -883,7 +882,7 @@ static hipError_t launch_dgq(const PartArgs &a, hipStream_t st) {
         case 0:
             // at d 128, pages holding whole tiles: loads straight into LDS
             if constexpr (D == 128)
-                hipLaunchKernelGGL((part_mfma_kernel<D, G, QW, 0, KS, NTL, true>), grid, dim3(256 * KS), 0, st, a);
+                hipLaunchKernelGGL((part_mfma_kernel<D, G, QW, 0, KS, NTL, true>), grid, dim3(640), 0, st, a);
             else
                 hipLaunchKernelGGL((part_mfma_kernel<D, G, QW, 0, KS, NTL, false>), grid, dim3(256 * KS), 0, st, a);
             break;
