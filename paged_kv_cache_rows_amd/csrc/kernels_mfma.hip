@@ -181,6 +181,10 @@ __device__ __forceinline__ v4i16_t lds_read_tr16(const char *p) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS v4i16_t *)(p));
 }
 
+// Loading waves of the d 128 direct-to-LDS kernel (a multiple of its 2 key sub-tiles): one
+// wave issues a 1 KB load about every 70 cycles, so a step's 64 loads need several of them.
+constexpr int kLoadWaves = 4;
+
 __device__ __forceinline__ f32x4_t mfma16(const bf16x8_t &a, const bf16x8_t &b, const f32x4_t &c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
@@ -203,11 +207,12 @@ __device__ __forceinline__ f32x4_t mfma16(const bf16x8_t &a, const bf16x8_t &b, 
 // comes from transposed 8-byte LDS reads (ds_read_b64_tr_b16): within each 16-lane group,
 // lane 4 a + e receives element e of the 8-byte pieces that lanes a, a + 4, a + 8 and a + 12
 // address, i.e. four consecutive keys of one channel when those lanes address four
-// consecutive rows.  Two more waves (a workgroup of 640 threads) issue all the loads: a CU's
-// vector memory path takes about 18 cycles per 1 KB load, so a burst of a step's 64 loads
-// would otherwise hold the computing waves at issue.
+// consecutive rows.  Four more waves (a workgroup of 768 threads) issue all the loads: a wave
+// issues a 1 KB load about every 70 cycles, so a burst of a step's 64 loads would otherwise
+// hold the computing waves at issue (two loading waves: the 2,048-token prompt 99.6 µs, four:
+// 97.8 µs; the verify window's cold part kernel 35.8 and 34.4 µs).
 template <int D, int G, int QW, int MODE, int KS, bool NTL, bool DMA>
-__global__ __launch_bounds__(DMA ? 640 : 256 * KS) void part_mfma_kernel(const PartArgs a) {
+__global__ __launch_bounds__(DMA ? 256 * KS + 64 * kLoadWaves : 256 * KS) void part_mfma_kernel(const PartArgs a) {
     using Geo = MfmaGeom<D>;
     constexpr int KT = Geo::KT, KRS = Geo::KRS, CB = Geo::CB, KPT = Geo::KPT, TC = Geo::TC;
     static_assert(!DMA || (D == 128 && MODE == 0 && KS == 2), "direct-to-LDS tiles: d 128, whole tiles per page");
@@ -218,7 +223,7 @@ __global__ __launch_bounds__(DMA ? 640 : 256 * KS) void part_mfma_kernel(const P
     constexpr int NCB = D / 16;      // 16-channel blocks (PV output blocks)
     constexpr int NPM = KT / 32;     // 32-key PV k-steps
 
-    constexpr int NTH = DMA ? 640 : 256 * KS;    // threads (with DMA: 8 computing waves and 2 loading)
+    constexpr int NTH = DMA ? 256 * KS + 64 * kLoadWaves : 256 * KS;   // threads (with DMA: 8 computing waves and the loading ones)
     static_assert((KS == 2) == (D == 128) && (KS == 1 || KS == 2), "key sub-tiles: 2 at D = 128, 1 at D = 256 and 512");
 
     // NBUF tile buffers: with two, a step stages the next step's tiles into one buffer while it
@@ -235,11 +240,13 @@ __global__ __launch_bounds__(DMA ? 640 : 256 * KS) void part_mfma_kernel(const P
     // (a sub-tile inside the split, a full tile) become scalar branches, not exec-mask ones
     const int wave = __builtin_amdgcn_readfirstlane((tid >> 6) & 3);   // column wave: query vectors 16 (wave QW + b) + col
     const int ksub = __builtin_amdgcn_readfirstlane(min(tid >> 8, KS - 1));   // key sub-tile this wave computes (and thread stages)
-    // DMA: waves 8 and 9 only load (wave 8 + p the sub-tiles p of every step), so that the
-    // computing waves never wait at the issue of a burst of loads while the CU's vector memory
-    // path drains it
+    // DMA: waves 8 .. 8 + kLoadWaves - 1 only load (wave 8 + p rows of sub-tile p / LPS of every
+    // step, LPS waves per sub-tile), so that the computing waves never wait at the issue of a
+    // burst of loads
     const bool producer = DMA && tid >= 512;
-    const int psub = __builtin_amdgcn_readfirstlane(producer ? (tid >> 6) - 8 : 0);
+    const int pw = __builtin_amdgcn_readfirstlane(producer ? (tid >> 6) - 8 : 0);
+    constexpr int LPS = kLoadWaves / KS;                 // loading waves per sub-tile
+    const int psub = pw / LPS, prow0 = (pw % LPS) * (KT / LPS);
     const int col = lane & 15, grp = lane >> 4;
     // work item: the dispatcher hands workgroups to the 8 XCDs round-robin (dispatch id
     // d goes to XCD d mod 8), so XCD x gets the contiguous items [x per, (x + 1) per), ordered
@@ -675,20 +682,20 @@ __global__ __launch_bounds__(DMA ? 640 : 256 * KS) void part_mfma_kernel(const P
                 const char *base = reinterpret_cast<const char *>(pages + (size_t)pg * page_elems + head_off +
                                                                   (size_t)(ts - idx * P) * D);
 #pragma unroll
-                for (int j = 0; j < KT / 4; ++j) {
-                    const int r = 4 * j + (lane >> 4);
+                for (int j = 0; j < KT / 4 / LPS; ++j) {
+                    const int r = prow0 + 4 * j + (lane >> 4);
                     const int piece = (lane & 15) ^ (is_v ? 2 * (r & 7) : (r & 15));
-                    load_to_lds<NTL>(base + r * 2 * D + 16 * piece, sub + j * 4 * 2 * D);
+                    load_to_lds<NTL>(base + r * 2 * D + 16 * piece, sub + (prow0 + 4 * j) * 2 * D);
                 }
             };
             auto pfix = [&](int it, char *sub) {
                 const int ts = kt_first + (it * KS + psub) * KT;
                 if (ts >= kend || (ts >= kbeg && ts + KT <= kend)) return;
 #pragma unroll
-                for (int j = 0; j < KT / 4; ++j) {
-                    const int key = ts + 4 * j + (lane >> 4);
+                for (int j = 0; j < KT / 4 / LPS; ++j) {
+                    const int key = ts + prow0 + 4 * j + (lane >> 4);
                     if (key < kbeg || key >= kend)
-                        *reinterpret_cast<u32x4 *>(sub + j * 4 * 2 * D + 16 * lane) = u32x4{0u, 0u, 0u, 0u};
+                        *reinterpret_cast<u32x4 *>(sub + (prow0 + 4 * j) * 2 * D + 16 * lane) = u32x4{0u, 0u, 0u, 0u};
                 }
             };
             pload(0, a.k_pages, pk0, false);
@@ -882,7 +889,8 @@ static hipError_t launch_dgq(const PartArgs &a, hipStream_t st) {
         case 0:
             // at d 128, pages holding whole tiles: loads straight into LDS
             if constexpr (D == 128)
-                hipLaunchKernelGGL((part_mfma_kernel<D, G, QW, 0, KS, NTL, true>), grid, dim3(640), 0, st, a);
+                hipLaunchKernelGGL((part_mfma_kernel<D, G, QW, 0, KS, NTL, true>), grid, dim3(256 * KS + 64 * kLoadWaves), 0,
+                                   st, a);
             else
                 hipLaunchKernelGGL((part_mfma_kernel<D, G, QW, 0, KS, NTL, false>), grid, dim3(256 * KS), 0, st, a);
             break;
