@@ -169,6 +169,25 @@ MfmaPlan mfma_plan(int D, int G, int R, int S, int Hkv, int P, int max_seq_len, 
 // alone): loads that write LDS directly have landed once it returns.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+// The loading waves' workgroup barrier: their LDS stores (zeroed rows) complete (lgkmcnt 0),
+// loads into LDS still in flight stay in flight (the loads a barrier publishes are waited for
+// explicitly before it).  A barrier with a workgroup release fence would wait for every load
+// that writes LDS.
+__device__ __forceinline__ void loader_barrier() {
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt 0
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// Waits until at most N of this wave's vector memory operations are outstanding (they complete
+// in issue order; expcnt and lgkmcnt left alone).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
 // 16 bytes per lane from global memory straight into LDS: lane l's bytes land at dst + 16 l
 // (dst wave-uniform).  NT: nontemporal.
 template <bool NT>
@@ -211,10 +230,14 @@ __device__ __forceinline__ f32x4_t mfma16(const bf16x8_t &a, const bf16x8_t &b, 
 // issues a 1 KB load about every 70 cycles, so a burst of a step's 64 loads would otherwise
 // hold the computing waves at issue (two loading waves: the 2,048-token prompt 99.6 µs, four:
 // 97.8 µs; the verify window's cold part kernel 35.8 and 34.4 µs).
-template <int D, int G, int QW, int MODE, int KS, bool NTL, bool DMA>
+template <int D, int G, int QW, int MODE, int KS, bool NTL, bool DMA, bool DEEP = false>
 __global__ __launch_bounds__(DMA ? 256 * KS + 64 * kLoadWaves : 256 * KS) void part_mfma_kernel(const PartArgs a) {
     using Geo = MfmaGeom<D>;
-    constexpr int KT = Geo::KT, KRS = Geo::KRS, CB = Geo::CB, KPT = Geo::KPT, TC = Geo::TC;
+    constexpr int KRS = Geo::KRS, CB = Geo::CB, KPT = Geo::KPT, TC = Geo::TC;
+    // DEEP (with DMA, split calls): 32-key sub-tiles in four buffers per operand, loaded two
+    // steps further ahead
+    static_assert(!DEEP || DMA, "deep prefetch loads straight into LDS");
+    constexpr int KT = DEEP ? 32 : Geo::KT;   // keys per sub-tile
     static_assert(!DMA || (D == 128 && MODE == 0 && KS == 2), "direct-to-LDS tiles: d 128, whole tiles per page");
     constexpr int KROW = DMA ? D : KRS;   // K tile row stride (bf16)
     constexpr int M = 64 * QW;       // query vectors per workgroup
@@ -228,7 +251,7 @@ __global__ __launch_bounds__(DMA ? 256 * KS + 64 * kLoadWaves : 256 * KS) void p
 
     // NBUF tile buffers: with two, a step stages the next step's tiles into one buffer while it
     // computes on the other (one barrier per step); one buffer stages and computes in turn
-    constexpr int NBUF = (KS == 2 || (D == 256 && MODE == 0)) ? 2 : 1;
+    constexpr int NBUF = DEEP ? 4 : (KS == 2 || (D == 256 && MODE == 0)) ? 2 : 1;
     __shared__ __attribute__((aligned(16))) uint16_t k_lds_all[NBUF][KS][KT * KROW];
     // V^T units, or with DMA the V rows of a tile (KT x D bf16, the same bytes)
     __shared__ __attribute__((aligned(16))) uint2 vt_lds_all[NBUF][KS][D * KT / 4];
@@ -698,6 +721,43 @@ __global__ __launch_bounds__(DMA ? 256 * KS + 64 * kLoadWaves : 256 * KS) void p
                         *reinterpret_cast<u32x4 *>(sub + (prow0 + 4 * j) * 2 * D + 16 * lane) = u32x4{0u, 0u, 0u, 0u};
                 }
             };
+            if constexpr (DEEP) {
+                // Four buffers per operand: in step j the computing waves read K(j + 1) and
+                // V(j), while K(j + 4) and V(j + 3) are issued into the buffers of K(j) and
+                // V(j - 1), and the wait is for K(j + 2) and V(j + 1), issued two steps before:
+                // the 4 newest groups of 4 loads of this wave may stay in flight (vmcnt 16) when
+                // all of them were issued in full, else every load is waited for.
+                auto kb = [&](int i) { return reinterpret_cast<char *>(k_lds_all[i & (NBUF - 1)][psub]); };
+                auto vb = [&](int i) { return reinterpret_cast<char *>(vt_lds_all[i & (NBUF - 1)][psub]); };
+                static_assert(KT / 4 / LPS == 4, "4 loads per wave, operand and step");
+                const bool ahead = nsteps >= 5;
+                pload(0, a.k_pages, kb(0), false);
+                pload(1, a.k_pages, kb(1), false);
+                pload(0, a.v_pages, vb(0), true);
+                pload(2, a.k_pages, kb(2), false);
+                pload(1, a.v_pages, vb(1), true);
+                pload(3, a.k_pages, kb(3), false);
+                pload(2, a.v_pages, vb(2), true);
+                if (ahead) wait_vmcnt<24>(); else wait_vmem();    // K(0)
+                loader_barrier();
+                if (ahead) wait_vmcnt<16>(); else wait_vmem();    // K(1), V(0)
+                pfix(0, vb(0));
+                loader_barrier();   // the computing waves' scores of step 0
+                for (int it = 0; it < nsteps; it += 2) {
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+                        const int j = it + h;
+                        pload(j + 4, a.k_pages, kb(j + 4), false);
+                        pload(j + 3, a.v_pages, vb(j + 3), true);
+                        if (j + 4 <= nsteps - 2) wait_vmcnt<16>(); else wait_vmem();   // K(j + 2), V(j + 1)
+                        pfix(j + 1, vb(j + 1));
+                        loader_barrier();
+                    }
+                }
+                lds_fence();   // the two barriers of the key groups' combine
+                lds_fence();
+                return;
+            }
             pload(0, a.k_pages, pk0, false);
             pload(1, a.k_pages, pk1, false);
             pload(0, a.v_pages, pv0, true);
@@ -726,11 +786,11 @@ __global__ __launch_bounds__(DMA ? 256 * KS + 64 * kLoadWaves : 256 * KS) void p
         qk(0, 0, s0);
         lds_fence();   // K buffer 0 is loaded again next
         for (int it = 0; it < nsteps; it += 2) {
-            qk(it + 1, 1, s1);
-            smpv(it, 0, s0);
+            qk(it + 1, (it + 1) & (NBUF - 1), s1);
+            smpv(it, it & (NBUF - 1), s0);
             lds_fence();
-            qk(it + 2, 0, s0);
-            smpv(it + 1, 1, s1);
+            qk(it + 2, (it + 2) & (NBUF - 1), s0);
+            smpv(it + 1, (it + 1) & (NBUF - 1), s1);
             lds_fence();
         }
     } else if constexpr (NBUF == 2) {
@@ -888,9 +948,15 @@ static hipError_t launch_dgq(const PartArgs &a, hipStream_t st) {
     switch (table_mode(a.P, a.chunk, Geo::KT, 1)) {
         case 0:
             // at d 128, pages holding whole tiles: loads straight into LDS
-            if constexpr (D == 128)
-                hipLaunchKernelGGL((part_mfma_kernel<D, G, QW, 0, KS, NTL, true>), grid, dim3(256 * KS + 64 * kLoadWaves), 0,
-                                   st, a);
+            if constexpr (D == 128) {
+                // split calls (verify windows) stream their keys from HBM: deeper prefetch
+                if (a.direct)
+                    hipLaunchKernelGGL((part_mfma_kernel<D, G, QW, 0, KS, NTL, true>), grid, dim3(256 * KS + 64 * kLoadWaves),
+                                       0, st, a);
+                else
+                    hipLaunchKernelGGL((part_mfma_kernel<D, G, QW, 0, KS, NTL, true, true>), grid,
+                                       dim3(256 * KS + 64 * kLoadWaves), 0, st, a);
+            }
             else
                 hipLaunchKernelGGL((part_mfma_kernel<D, G, QW, 0, KS, NTL, false>), grid, dim3(256 * KS), 0, st, a);
             break;

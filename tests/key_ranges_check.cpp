@@ -249,6 +249,8 @@ void check_mfma(const Shape &c, const CallPlan &p, const Table &t, int Ldev) {
     const int L = kernel_len(Ldev, c.max_len);
     if (Ldev > c.max_len && L != c.max_len) report(c, Ldev, "length above max_seq_len not read as max_seq_len", L, c.max_len);
     if (L <= 0) return;
+    // (at d 128 in table mode 0 the kernel of a split call walks 32-key halves of these tiles;
+    // with pages a multiple of 64 keys they read the same rows through the same pages)
     const int KT = mfma_tile_keys(c.D);
     const int mode = mfma_table_mode(c.D, c.P, p.chunk);
     const int stride = t.stride;
