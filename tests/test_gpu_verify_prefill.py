@@ -56,6 +56,21 @@ def test_verify_splits_of_many_step_counts(L, P):
     assert_close(attend("verify", c, q), oracle_for(c, q), f"verify L={L} P={P}")
 
 
+@pytest.mark.parametrize("L", [2300, 2700, 3100, 3600, 4100])
+@pytest.mark.parametrize("P", [64, 512])
+@pytest.mark.parametrize("W", [0, 77])
+def test_verify_split_pipeline_depths(L, P, W):
+    # pages a multiple of 64 keys: the split calls' kernel with 32-key sub-tiles in four buffers
+    # per operand.  Chunks of about L / 8 keys give 5 to 9 steps of 64 keys, where its loads
+    # stay in flight across barriers only while four more groups of them have been issued in
+    # full; a window of 77 starts each row's keys off a sub-tile boundary
+    w = _w(streams=4, kv_heads=8, group=8, rows=8, page_size=P, lengths=[L, L - 45, L // 2 + 3, 9])
+    say(f"verify split pipeline L={L} P={P} W={W}")
+    c, _, _ = new_cache(w)
+    q = workloads.queries(w).cuda()
+    assert_close(attend("verify", c, q, window=W), oracle_for(c, q, W), f"verify L={L} P={P} W={W}")
+
+
 @pytest.mark.parametrize("entry,R,G,D,Hkv", [("decode", 1, 8, 128, 2), ("verify", 3, 4, 128, 2),
                                               ("verify", 8, 8, 128, 2), ("verify", 4, 8, 512, 1),
                                               ("prefill", 100, 4, 128, 2), ("prefill", 512, 4, 128, 8)])
