@@ -318,6 +318,40 @@ def read_ceiling(torch, setup, flush, iters=10, grid=2048):
                     f"loads), a 1 GiB flush before each of {iters} calls"}
 
 
+_READ_BUF = {}
+
+
+def same_size_read(torch, nbytes, flush, iters=10, grids=(512, 1024, 2048, 4096)):
+    """The cold read rate of a plain streaming read (libkvprobe.so) of `nbytes` contiguous bytes,
+    timed as the cold attention calls are (a flush before each call, events around it): the
+    best median over a few grid sizes.  At tens of MB the launch, the first round trips and the
+    drain weigh on any kernel, so this, not the long-read ceiling, is what a workload of that
+    size can approach."""
+    lib = ctypes.CDLL(PROBE_LIB)
+    lib.kvprobe_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    lib.kvprobe_read.restype = ctypes.c_int
+    n = nbytes // 16 * 16
+    if _READ_BUF.get("t") is None or _READ_BUF["t"].numel() * 2 < n:
+        _READ_BUF["t"] = None
+        _READ_BUF["t"] = torch.ones((n + 1) // 2, dtype=torch.int16, device="cuda")
+    buf = _READ_BUF["t"]
+    stream = torch.cuda.current_stream().cuda_stream
+    best = None
+    for grid in grids:
+        sink = torch.zeros(grid, dtype=torch.int32, device="cuda")
+
+        def probe():
+            rc = lib.kvprobe_read(buf.data_ptr(), n, grid, sink.data_ptr(), stream)
+            if rc != 0:
+                raise RuntimeError(f"kvprobe_read failed: {rc}")
+        probe()
+        ms, _ = cold_calls(probe, iters, torch, flush)
+        med = stats_us(ms)["median"]
+        if best is None or med < best[0]:
+            best = (med, grid)
+    return {"us": round(best[0], 2), "GBps": round(n / (best[0] * 1e-6) / 1e9, 1), "grid": best[1]}
+
+
 def cold_record(ms, kv_bytes, flops=None, part_ms=None):
     st = stats_us(ms)
     rec = {"cold_us": st, "cold_kv_GBps": round(kv_bytes / (st["median"] * 1e-6) / 1e9, 1),
@@ -341,6 +375,15 @@ def other_workloads(torch, binding, staging, workloads, flush, cases):
     res = {}
     iters = 20
 
+    def vs_read(rec, nbytes):
+        """rec plus the same-size streaming read and the cold times' rate as a fraction of it"""
+        ceil = same_size_read(torch, nbytes, flush)
+        rec["same_size_read"] = ceil
+        rec["cold_vs_read"] = round(ceil["us"] / rec["cold_us"]["median"], 3)
+        if "cold_part_us" in rec:
+            rec["cold_part_vs_read"] = round(ceil["us"] / rec["cold_part_us"]["median"], 3)
+        return rec
+
     # tiny decode: 1 stream, 300 keys in pages of 64 (5 of an 8-page pool)
     w = workloads.tiny_decode()
     c = staging.make_cache(w, order=workloads.free_order(w.pool_pages, 3001))
@@ -352,7 +395,7 @@ def other_workloads(torch, binding, staging, workloads, flush, cases):
     warm = graph_us(call, torch, check=out)
     ms, _ = cold_calls(call, iters, torch, flush)
     by = sum(c.lengths) * w.kv_bytes_per_token
-    res["tiny_decode_300"] = {"warm_us": round(warm, 2), "kv_bytes": by, **cold_record(ms, by)}
+    res["tiny_decode_300"] = vs_read({"warm_us": round(warm, 2), "kv_bytes": by, **cold_record(ms, by)}, by)
     cases.append({"name": "tiny_decode_300", "q": q, "ks": ks, "vs": vs, "lengths": c.lengths, "window": 0,
                   "out": out.clone()})
 
@@ -370,10 +413,10 @@ def other_workloads(torch, binding, staging, workloads, flush, cases):
     ms, pms = cold_calls(call, iters, torch, flush, part=True, binding=binding)
     by = sum(c.lengths) * w.kv_bytes_per_token
     fl = attn_flops(c.lengths, w.rows, w.q_heads, w.head_dim)
-    res["verify_window_4x8rows_9k"] = {"warm_us": round(warm, 2),
-                                       "warm_kv_GBps": round(by / warm / 1e3, 1),
-                                       "warm_TFLOPs": round(fl / warm / 1e6, 2),
-                                       "kv_bytes": by, "flops": fl, **cold_record(ms, by, fl, pms)}
+    res["verify_window_4x8rows_9k"] = vs_read({"warm_us": round(warm, 2),
+                                               "warm_kv_GBps": round(by / warm / 1e3, 1),
+                                               "warm_TFLOPs": round(fl / warm / 1e6, 2),
+                                               "kv_bytes": by, "flops": fl, **cold_record(ms, by, fl, pms)}, by)
     cases.append({"name": "verify_window_4x8rows_9k", "q": q, "ks": ks, "vs": vs, "lengths": c.lengths,
                   "window": 0, "out": out.clone()})
     # the same window as a flattened draft tree (seeded random trees, parents before children)
@@ -392,7 +435,7 @@ def other_workloads(torch, binding, staging, workloads, flush, cases):
     call = lambda: binding.verify_tree(c.pool, q, c.table, c.seq_len, c.max_seq_len, tm, out=out_t, workspace=ws)
     warm = graph_us(call, torch, check=out_t)
     ms, _ = cold_calls(call, iters, torch, flush)
-    res["verify_tree_4x8rows_9k"] = {"warm_us": round(warm, 2), **cold_record(ms, by)}
+    res["verify_tree_4x8rows_9k"] = vs_read({"warm_us": round(warm, 2), **cold_record(ms, by)}, by)
     cases.append({"name": "verify_tree_4x8rows_9k", "q": q, "ks": ks, "vs": vs, "lengths": c.lengths,
                   "window": 0, "masks": masks, "out": out_t.clone()})
 
@@ -414,9 +457,9 @@ def other_workloads(torch, binding, staging, workloads, flush, cases):
     ms1, p1 = cold_calls(call1, iters, torch, flush, part=True, binding=binding)
     b0, b1 = c.lengths[0] * w.kv_bytes_per_token, c.lengths[1] * w.kv_bytes_per_token
     res["wide_head_d512_p37"] = {
-        "decode_2048": {"warm_us": round(w0, 2), "kv_bytes": b0, **cold_record(ms0, b0, None, p0)},
-        "verify4_9000": {"warm_us": round(w1, 2), "kv_bytes": b1,
-                         **cold_record(ms1, b1, attn_flops([9000], 4, w.q_heads, 512), p1)}}
+        "decode_2048": vs_read({"warm_us": round(w0, 2), "kv_bytes": b0, **cold_record(ms0, b0, None, p0)}, b0),
+        "verify4_9000": vs_read({"warm_us": round(w1, 2), "kv_bytes": b1,
+                                 **cold_record(ms1, b1, attn_flops([9000], 4, w.q_heads, 512), p1)}, b1)}
     cases.append({"name": "wide_head_decode_2048", "q": q0, "ks": ks[:1], "vs": vs[:1], "lengths": c.lengths[:1],
                   "window": 0, "out": o0.clone()})
     cases.append({"name": "wide_head_verify4_9000", "q": q1, "ks": ks[1:], "vs": vs[1:], "lengths": c.lengths[1:],
@@ -440,9 +483,9 @@ def other_workloads(torch, binding, staging, workloads, flush, cases):
     msv, pv = cold_calls(callv, iters, torch, flush, part=True, binding=binding)
     b = sum(c.lengths) * w.kv_bytes_per_token
     res["head_dim_256"] = {
-        "decode_4x16384": {"warm_us": round(wd, 2), "kv_bytes": b, **cold_record(msd, b, None, pd)},
-        "verify4_4x16384": {"warm_us": round(wv, 2), "kv_bytes": b,
-                            **cold_record(msv, b, attn_flops(c.lengths, 4, w.q_heads, 256), pv)}}
+        "decode_4x16384": vs_read({"warm_us": round(wd, 2), "kv_bytes": b, **cold_record(msd, b, None, pd)}, b),
+        "verify4_4x16384": vs_read({"warm_us": round(wv, 2), "kv_bytes": b,
+                                    **cold_record(msv, b, attn_flops(c.lengths, 4, w.q_heads, 256), pv)}, b)}
     cases.append({"name": "head_dim_256_decode", "q": qd, "ks": ks, "vs": vs, "lengths": c.lengths, "window": 0,
                   "out": od.clone()})
     cases.append({"name": "head_dim_256_verify4", "q": qv, "ks": ks, "vs": vs, "lengths": c.lengths, "window": 0,
@@ -477,6 +520,7 @@ def other_workloads(torch, binding, staging, workloads, flush, cases):
         for i, c0 in enumerate(range(0, 2048, 512)):
             cases.append({"name": f"{name}_chunk{i}", "q": qs[i], "ks": ks, "vs": vs, "lengths": [c0 + 512],
                           "window": window, "out": outs[i].clone(), "group": name})
+    _READ_BUF.clear()
     return res
 
 
