@@ -409,6 +409,26 @@ __global__ __launch_bounds__(DMA ? 256 * KS + 64 * kLoadWaves : 256 * KS) void p
             const size_t base = (size_t)pg * page_elems + head_off + (size_t)(tb - idx * P + KPT * kq) * D + 8 * kc;
 #pragma unroll
             for (int u = 0; u < KPT; ++u) r[u] = ld16(pages + base + (size_t)u * D);
+        } else if (MODE == 1 && D == 512 && P >= KPT) {
+            // the thread's KPT consecutive keys lie in at most two pages: one division and two
+            // table lookups serve all of them.  A d 512 workgroup runs one wave per SIMD, with
+            // nothing to hide a per-key division and 64-bit address behind (the 4-row verify at
+            // 9,000 keys over pages of 37: warm 27.1 -> 25.4 us, cold part kernel 28.9 -> 28.0);
+            // at d 128, two waves per SIMD, the per-key form measured faster (51.1 against
+            // 53.7 us over pages of 37).
+            const int j0 = tb + KPT * kq;
+            const int i0 = j0 / P;
+            const int off0 = j0 - i0 * P;
+            const uint16_t *const pa =
+                pages + (size_t)cached_page<TC>(t_lds, i0 - idx0) * page_elems + head_off + 8 * kc;
+            const uint16_t *const pb =
+                pages + (size_t)cached_page<TC>(t_lds, i0 + 1 - idx0) * page_elems + head_off + 8 * kc;
+#pragma unroll
+            for (int u = 0; u < KPT; ++u) {
+                const int off = off0 + u;
+                const bool next = off >= P;
+                r[u] = ld16((next ? pb : pa) + (next ? off - P : off) * D);
+            }
         } else {
 #pragma unroll
             for (int u = 0; u < KPT; ++u) {
