@@ -520,6 +520,26 @@ def other_workloads(torch, binding, staging, workloads, flush, cases):
         for i, c0 in enumerate(range(0, 2048, 512)):
             cases.append({"name": f"{name}_chunk{i}", "q": qs[i], "ks": ks, "vs": vs, "lengths": [c0 + 512],
                           "window": window, "out": outs[i].clone(), "group": name})
+
+        # the same prompt with each chunk's row write fused into its prefill (one launch per
+        # chunk); the rows it writes are the ones already there, byte for byte
+        outs_f = [torch.empty_like(x) for x in qs]
+
+        def prompt_fused():
+            for i in range(4):
+                binding.prefill_put(c.pool, qs[i], c.table, seqs[i], 2048, kn[i], vn[i], window=window,
+                                    ring_pages=c.ring_pages, out=outs_f[i])
+        warm_f = graph_us(prompt_fused, torch, reps=5, check=outs_f[3])
+        ms_f, _ = cold_calls(prompt_fused, iters, torch, flush)
+        res[name + "_fused_row_writes"] = {
+            "warm_us": round(warm_f, 2), "warm_us_per_chunk": round(warm_f / 4, 2),
+            "warm_TFLOPs": round(fl / warm_f / 1e6, 2),
+            "warm_mfma_frac": round(fl / warm_f / 1e6 / MFMA_BF16_PEAK_TFLOPS, 4), "flops": fl,
+            "kv_bytes": by, **cold_record(ms_f, by, fl),
+            "entry": "paged_attn_prefill_put per chunk (kv_rows_put + paged_attn_prefill in one launch)"}
+        for i, c0 in enumerate(range(0, 2048, 512)):
+            cases.append({"name": f"{name}_fused_chunk{i}", "q": qs[i], "ks": ks, "vs": vs, "lengths": [c0 + 512],
+                          "window": window, "out": outs_f[i].clone(), "group": name + "_fused_row_writes"})
     _READ_BUF.clear()
     return res
 

@@ -224,8 +224,9 @@ kv_status paged_attn_decode(const kv_pool *pool, const kv_layout *lay, const kv_
 /* kv_rows_put of one new row per stream followed by paged_attn_decode (TensorFold PR #1620,
  * opening description, Writes and Reads bullets: a layer's new K/V row is copied into the
  * pages, then attention reads through the table), in one launch where the group has fewer than
- * 16 query heads (the VALU kernel writes the row itself), else as a row-write launch followed
- * by the attention on the same stream.  k_new, v_new: device
+ * 16 query heads (the VALU kernel writes the row itself) or, with 16, at head_dim 128 over
+ * pages of a multiple of 64 positions (as paged_attn_prefill_put), else as a row-write launch
+ * followed by the attention on the same stream.  k_new, v_new: device
  * bf16 [S][1][Hkv][D] (16-byte aligned), written at position seq_len[s] - 1 exactly as
  * kv_rows_put writes it; the output and every byte of the pool afterwards equal those of the
  * two calls.  Errors as for decode, with KV_E_ARG for a null or misaligned k_new or v_new. */
@@ -272,6 +273,22 @@ kv_status paged_attn_verify_tree(const kv_pool *pool, const kv_layout *lay, cons
  * Errors as for decode, with KV_E_ARG for R < 1. */
 kv_status paged_attn_prefill(const kv_pool *pool, const kv_layout *lay, const kv_attn_args *a,
                              void *hip_stream);
+
+/* kv_rows_put of a prompt chunk's R rows followed by paged_attn_prefill (TensorFold PR #1620,
+ * opening description, Writes and Reads bullets), in one launch where the call runs the MFMA
+ * kernel at head_dim 128 over pages of a multiple of 64 positions (R times the group at least
+ * 16: every prompt chunk of that shape), or where R = 1 on the VALU kernel; otherwise as a
+ * row-write launch followed by the attention on the same stream.  In the one-launch form each
+ * new row is written into its page slot by one workgroup, and the attention reads the call's
+ * own rows from k_new and v_new rather than from those slots.  k_new, v_new: device bf16
+ * [S][R][Hkv][D] (16-byte aligned, caller-owned), row r of stream s written at position
+ * seq_len[s] - R + r exactly as kv_rows_put writes it (rows before position 0, or whose table
+ * entry is out of range, are skipped).  With every new row's table entry in range, the
+ * output and every byte of the pool afterwards equal those of the two calls.  A ring layer
+ * needs room for window + R - 1 positions, as for the two calls.  Errors as for prefill, with
+ * KV_E_ARG for a null or misaligned k_new or v_new. */
+kv_status paged_attn_prefill_put(const kv_pool *pool, const kv_layout *lay, const kv_attn_args *a,
+                                 const void *k_new, const void *v_new, void *hip_stream);
 
 /* Measurement hook: when both are non-NULL, every later attention call made by this thread
  * records hipEvent_t `start` on its stream just before its part kernel (the one that streams K

@@ -31,7 +31,7 @@ EXPORTS = ("kv_pool_create", "kv_pool_destroy", "kv_page_lease", "kv_page_releas
            "kv_pool_set_lease_policy",
            "kv_pool_free_count", "kv_stream_pages", "kv_rows_put", "kv_pages_copy", "paged_attn_workspace_size",
            "paged_attn_decode", "paged_attn_decode_put", "paged_attn_decode_put_static", "paged_attn_verify", "paged_attn_verify_tree",
-           "paged_attn_prefill",
+           "paged_attn_prefill", "paged_attn_prefill_put",
            "kv_set_part_events",
            "kv_last_error", "kv_abi_version")
 
@@ -90,6 +90,7 @@ def load(path: str = LIB_PATH):
         "paged_attn_verify": [c_void_p, POINTER(Layout), POINTER(AttnArgs), c_void_p],
         "paged_attn_verify_tree": [c_void_p, POINTER(Layout), POINTER(AttnArgs), c_void_p, c_void_p],
         "paged_attn_prefill": [c_void_p, POINTER(Layout), POINTER(AttnArgs), c_void_p],
+        "paged_attn_prefill_put": [c_void_p, POINTER(Layout), POINTER(AttnArgs), c_void_p, c_void_p, c_void_p],
         "kv_set_part_events": [c_void_p, c_void_p],
     }
     for name, args in sig.items():
@@ -329,6 +330,16 @@ def verify_tree(pool, q, table, seq_len, max_seq_len, tree_mask: torch.Tensor, *
 def prefill(pool, q, table, seq_len, max_seq_len, **kw):
     """paged_attn_prefill: a prompt chunk of any number of causal rows per stream."""
     return _attend("paged_attn_prefill", pool, q, table, seq_len, max_seq_len, **kw)
+
+
+def prefill_put(pool, q, table, seq_len, max_seq_len, k_new: torch.Tensor, v_new: torch.Tensor, **kw):
+    """paged_attn_prefill_put: write the chunk's rows k_new/v_new [S][R][Hkv][D] at positions
+    seq_len - R .. seq_len - 1 and attend (the same result as rows_put followed by prefill)."""
+    shape = (int(q.shape[0]), int(q.shape[1]), pool.kv_heads, pool.head_dim)
+    _need(k_new, torch.bfloat16, "k_new", shape)
+    _need(v_new, torch.bfloat16, "v_new", shape)
+    return _attend("paged_attn_prefill_put", pool, q, table, seq_len, max_seq_len,
+                   extra=(_ptr(k_new), _ptr(v_new)), **kw)
 
 
 def set_part_events(start: int | None, stop: int | None):

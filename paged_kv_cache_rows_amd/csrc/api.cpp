@@ -28,6 +28,12 @@ struct kv_pool {
     std::vector<std::vector<int32_t>> leased;
 };
 
+namespace kvp {
+// kernels_mfma.hip: whether the MFMA kernel a call of this shape runs writes and reads the
+// call's own new rows itself (the direct-to-LDS kernel)
+bool mfma_fuses_rows(int D, int P, int chunk);
+}  // namespace kvp
+
 namespace {
 
 thread_local std::string g_last_error;
@@ -215,9 +221,12 @@ kv_status run_attention(const kv_pool *pool, const kv_layout *lay, const kv_attn
     const float scale = a->scale > 0.f ? a->scale : 1.0f / std::sqrt((float)p.D);
     pa.scale_log2 = scale * 1.4426950408889634f;
 
-    if (k_new && p.cp.mfma) {
-        // the MFMA kernel has no fused row write: the row goes in first with the row-write
-        // kernel, on the same stream, so the attention reads it as kv_rows_put would leave it
+    // The new rows go in with the attention where its kernel writes them itself: the VALU
+    // kernel for one row per stream, the direct-to-LDS MFMA kernel for any rows.  Otherwise
+    // they go in first with the row-write kernel, on the same stream, so that the attention
+    // reads them as kv_rows_put leaves them.
+    const bool fused = p.cp.mfma ? kvp::mfma_fuses_rows(p.D, pool->page_size, p.cp.mp.chunk) : p.R == 1;
+    if (k_new && !fused) {
         pa.k_new = pa.v_new = nullptr;
         const hipError_t e = kvp::launch_rows_put(rows_args(pool, lay, k_new, v_new), hs);
         if (e != hipSuccess) return fail(KV_E_DEVICE, "%s: row-write launch failed: %s", who, hipGetErrorString(e));
@@ -595,6 +604,13 @@ kv_status paged_attn_verify_tree(const kv_pool *pool, const kv_layout *lay, cons
 kv_status paged_attn_prefill(const kv_pool *pool, const kv_layout *lay, const kv_attn_args *a, void *hip_stream) {
     if (lay && lay->rows < 1) return fail(KV_E_ARG, "paged_attn_prefill: rows %d < 1", lay->rows);
     return run_attention(pool, lay, a, hip_stream, "paged_attn_prefill");
+}
+
+kv_status paged_attn_prefill_put(const kv_pool *pool, const kv_layout *lay, const kv_attn_args *a,
+                                 const void *k_new, const void *v_new, void *hip_stream) {
+    if (lay && lay->rows < 1) return fail(KV_E_ARG, "paged_attn_prefill_put: rows %d < 1", lay->rows);
+    if (!k_new || !v_new) return fail(KV_E_ARG, "paged_attn_prefill_put: k_new or v_new is null");
+    return run_attention(pool, lay, a, hip_stream, "paged_attn_prefill_put", nullptr, k_new, v_new);
 }
 
 kv_status kv_set_part_events(void *start_event, void *stop_event) {

@@ -75,6 +75,10 @@ __device__ __forceinline__ int vt_unit(int ch, int kg) {
     return sr * 32 + ((rr * Geo::UPR + kg) ^ vt_swz(sr));
 }
 
+// Whether a call of this shape runs the direct-to-LDS kernel, which fuses the row write of
+// its own rows (PartArgs::k_new / v_new); the other MFMA kernels ignore k_new.
+bool mfma_fuses_rows(int D, int P, int chunk) { return D == 128 && table_mode(P, chunk, MfmaGeom<128>::KT, 1) == 0; }
+
 int mfma_tile_keys(int D) { return D == 512 ? MfmaGeom<512>::KT : D == 256 ? MfmaGeom<256>::KT : MfmaGeom<128>::KT; }
 int mfma_table_mode(int D, int P, int chunk) { return table_mode(P, chunk, mfma_tile_keys(D), 1); }
 
@@ -331,6 +335,34 @@ __global__ __launch_bounds__(DMA ? 256 * KS + 64 * kLoadWaves : 256 * KS) void p
         }
     }
 
+    // The call's own rows go in with the attention (kv_rows_put fused, direct-to-LDS kernel):
+    // split 0 of the tile in which a row's first query vector lies writes that row's K and V of
+    // head kvh into its page slot, exactly as kv_rows_put does, and every workgroup reads the
+    // call's rows from k_new and v_new, never from those slots.  The slots written hold
+    // positions that no row of the call sees (the ring holds at least window + R - 1
+    // positions, as for kv_rows_put followed by the attention), so no workgroup reads what
+    // another writes.  The loading waves do it once their last loads are issued, while the
+    // computing waves finish the last steps.
+    auto put_rows = [&](int t, int nt_) {
+        if (a.k_new == nullptr || split != 0) return;
+        constexpr int PPR = D / 8;                     // 16-byte pieces of a row
+        const int rb = (v0 + G - 1) / G, re = min((v0 + M + G - 1) / G, R);
+        for (int w = t; w < (re - rb) * 2 * PPR; w += nt_) {
+            const int rr = rb + w / (2 * PPR), op = (w / PPR) & 1, pc = w % PPR;
+            const int pos = L - R + rr;
+            if (pos < 0) continue;
+            int idx = pos / a.P;
+            const int off = pos - idx * a.P;
+            if (a.ring_pages) idx %= a.ring_pages;
+            if (idx >= a.stride) continue;
+            const int pg = trow[idx];
+            if ((unsigned)pg >= (unsigned)a.num_pages) continue;
+            const uint16_t *src = (op ? a.v_new : a.k_new) + ((size_t)(s * R + rr) * a.Hkv + kvh) * D + 8 * pc;
+            uint16_t *dst = const_cast<uint16_t *>(op ? a.v_pages : a.k_pages) +
+                            (((size_t)pg * a.Hkv + kvh) * a.P + off) * D + 8 * pc;
+            *reinterpret_cast<u32x4 *>(dst) = *reinterpret_cast<const u32x4 *>(src);
+        }
+    };
     const int r_first = v0 / G;
     const int r_last = (min(NQ, v0 + M) - 1) / G;
     const int p_first = L - R + r_first, p_last = L - R + r_last;
@@ -352,6 +384,7 @@ __global__ __launch_bounds__(DMA ? 256 * KS + 64 * kLoadWaves : 256 * KS) void p
                 }
             }
         }
+        if constexpr (DMA) put_rows(tid, NTH);
         return;
     }
     const int lo_full = W > 0 ? p_last - W + 1 : 0;   // every column sees keys >= this ...
@@ -717,6 +750,10 @@ __global__ __launch_bounds__(DMA ? 256 * KS + 64 * kLoadWaves : 256 * KS) void p
             // which a zero weight would not cancel)
             char *const pk0 = reinterpret_cast<char *>(k_lds_all[0][psub]), *const pk1 = reinterpret_cast<char *>(k_lds_all[1][psub]);
             char *const pv0 = reinterpret_cast<char *>(vt_lds_all[0][psub]), *const pv1 = reinterpret_cast<char *>(vt_lds_all[1][psub]);
+            // with the row write fused, keys from L - R on (the call's own rows) come from
+            // k_new / v_new [S][R][Hkv][D]; a key past the stream (tail of the last sub-tile,
+            // masked) rereads row R - 1
+            const int new0 = L - R;
             auto pload = [&](int it, const uint16_t *pages, char *sub, bool is_v) {
                 const int ts = kt_first + (it * KS + psub) * KT;
                 if (ts >= kend) return;
@@ -724,6 +761,21 @@ __global__ __launch_bounds__(DMA ? 256 * KS + 64 * kLoadWaves : 256 * KS) void p
                 const int pg = __builtin_amdgcn_readfirstlane(cached_page<TC>(t_lds, idx - idx0));
                 const char *base = reinterpret_cast<const char *>(pages + (size_t)pg * page_elems + head_off +
                                                                   (size_t)(ts - idx * P) * D);
+                if (a.k_new != nullptr && ts + KT > new0) {
+                    const char *nb = reinterpret_cast<const char *>((is_v ? a.v_new : a.k_new) +
+                                                                    ((size_t)s * R * a.Hkv + kvh) * D);
+#pragma unroll
+                    for (int j = 0; j < KT / 4 / LPS; ++j) {
+                        const int r = prow0 + 4 * j + (lane >> 4);
+                        const int piece = (lane & 15) ^ (is_v ? 2 * (r & 7) : (r & 15));
+                        const int key = ts + r;
+                        const char *src = key >= new0
+                                              ? nb + (size_t)min(key - new0, R - 1) * a.Hkv * 2 * D + 16 * piece
+                                              : base + r * 2 * D + 16 * piece;
+                        load_to_lds<NTL>(src, sub + (prow0 + 4 * j) * 2 * D);
+                    }
+                    return;
+                }
 #pragma unroll
                 for (int j = 0; j < KT / 4 / LPS; ++j) {
                     const int r = prow0 + 4 * j + (lane >> 4);
@@ -774,6 +826,7 @@ __global__ __launch_bounds__(DMA ? 256 * KS + 64 * kLoadWaves : 256 * KS) void p
                         loader_barrier();
                     }
                 }
+                put_rows(tid - 512, 64 * kLoadWaves);
                 lds_fence();   // the two barriers of the key groups' combine
                 lds_fence();
                 return;
@@ -797,6 +850,7 @@ __global__ __launch_bounds__(DMA ? 256 * KS + 64 * kLoadWaves : 256 * KS) void p
                 pfix(it + 2, pv0);
                 lds_fence();
             }
+            put_rows(tid - 512, 64 * kLoadWaves);
             lds_fence();   // the two barriers of the key groups' combine
             lds_fence();
             return;

@@ -15,13 +15,17 @@
 //   * the merge of each row combines only splits that were written and that hold all of the
 //     row's keys;
 //   * the fused decode row write finds the page of position L - 1;
+//   * with a prompt chunk's row write fused into the MFMA kernel, every new row is written by
+//     exactly one workgroup, into the page the table gives for its position, and no key a
+//     workgroup reads from the pages shares its slot with a row the call writes;
 //   * a device length above max_seq_len is read as max_seq_len.
 // Streams at the longest length a call may describe (KV_MAX_SEQ_LEN) are checked for their
 // ranges and merge spans only (no row walk): the checker is built with the signed-overflow
 // check of UndefinedBehaviorSanitizer, so any 32-bit overflow in the shared range functions
 // aborts it.
-// `--plant merge` drops the last split of every merge span and `--plant cache` shrinks the
-// checker's idea of the table cache by one entry: both must be reported.  `--plant overflow`
+// `--plant merge` drops the last split of every merge span, `--plant cache` shrinks the
+// checker's idea of the table cache by one entry and `--plant put` starts each tile's fused
+// row write one row late: each must be reported.  `--plant overflow`
 // feeds split_piece a length past the limit: the sanitizer must stop the run.
 //
 // Exit status 0 and a line "violations 0" when every check holds.
@@ -39,6 +43,11 @@
 #include <vector>
 
 using namespace kvp;
+
+namespace kvp {
+// kernels_mfma.hip: whether a call of this shape runs the kernel that writes its own new rows
+bool mfma_fuses_rows(int D, int P, int chunk);
+}  // namespace kvp
 
 namespace {
 
@@ -258,9 +267,28 @@ void check_mfma(const Shape &c, const CallPlan &p, const Table &t, int Ldev) {
     const int NQ = c.R * c.G, M = 64 * p.mp.qw;
     if (p.chunk % KT != 0) report(c, L, "chunk not a whole number of tiles", p.chunk, KT);
     if (p.mp.tiles * M < NQ) report(c, L, "query tiles do not cover the vectors", p.mp.tiles, NQ);
+    // the fused row write: split 0 of the tile holding a row's first query vector writes it
+    const bool fused = mfma_fuses_rows(c.D, c.P, p.chunk);
+    const int new0 = L - c.R, cap = c.ring * c.P;
+    std::vector<int> writers(fused ? c.R : 0, 0);
     for (int tile = 0; tile < p.mp.tiles; ++tile) {
         const int v0 = tile * M;
         if (v0 >= NQ) continue;
+        if (fused) {
+            // `--plant put`: each tile's write starts one row late
+            const int rb = (v0 + c.G - 1) / c.G + (plant == "put" ? 1 : 0);
+            const int re = std::min((v0 + M + c.G - 1) / c.G, c.R);
+            for (int r = rb; r < re; ++r) {
+                ++writers[r];
+                const int pos = new0 + r;
+                if (pos < 0 || !walk_rows) continue;
+                int idx = pos / c.P;
+                if (c.ring) idx %= c.ring;
+                const int pg = idx < stride ? t.e[idx] : -1;
+                if (pg >= 0 && pg < t.num_pages && pg != true_page(c, t, pos))
+                    report(c, L, "fused row write to the wrong page", pos, pg);
+            }
+        }
         const int r_first = v0 / c.G, r_last = (std::min(NQ, v0 + M) - 1) / c.G;
         const int p_first = L - c.R + r_first, p_last = L - c.R + r_last;
         const int lo_tile = c.window > 0 ? std::max(0, p_first - c.window + 1) : 0;
@@ -275,6 +303,14 @@ void check_mfma(const Shape &c, const CallPlan &p, const Table &t, int Ldev) {
             written[split] = 1;
             if (k.kend - k.c0 > p.chunk) report(c, L, "chunk overrun", k.kend - k.c0, p.chunk);
             cover.push_back({k.kbeg, k.kend});
+            if (fused && cap > 0) {
+                // keys read from the pages: [kbeg, min(kend, new0)); a written position p
+                // shares the slot of key p - cap, so none of [kbeg + cap, min(kend, new0) + cap)
+                // may be one of [max(new0, 0), L)
+                const int64_t a0 = std::max<int64_t>((int64_t)k.kbeg + cap, std::max(new0, 0));
+                const int64_t a1 = std::min<int64_t>((int64_t)std::min(k.kend, new0) + cap, L);
+                if (a0 < a1) report(c, L, "a key read from the pages shares its slot with a written row", k.kbeg, a0);
+            }
             if (!walk_rows) continue;
             const int kt_first = (k.kbeg / KT) * KT;
             const int nt = (k.kend - kt_first + KT - 1) / KT;
@@ -316,6 +352,8 @@ void check_mfma(const Shape &c, const CallPlan &p, const Table &t, int Ldev) {
             if (!tiles_exactly(got, lo_r, pos + 1)) report(c, L, "merge does not hold each key of its row once", pos, lo_r);
         }
     }
+    for (int r = 0; r < (int)writers.size(); ++r)
+        if (writers[r] != 1) report(c, L, "a new row is not written exactly once", r, writers[r]);
 }
 
 void check_shape(const Shape &c, std::mt19937 &rng) {

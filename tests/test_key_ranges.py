@@ -59,7 +59,8 @@ def test_every_workgroup_reads_its_own_pages_and_the_pieces_tile_the_keys(checke
 
 
 @pytest.mark.parametrize("plant, message", [("merge", "merge does not hold each key of its row once"),
-                                            ("cache", "used key read through an absent entry")])
+                                            ("cache", "used key read through an absent entry"),
+                                            ("put", "a new row is not written exactly once")])
 def test_planted_mistakes_are_reported(checker, plant, message):
     r, (*_, bad) = _run(checker, "--plant", plant)
     assert r.returncode == 1 and bad > 0 and message in r.stdout, r.stdout[-2000:]
