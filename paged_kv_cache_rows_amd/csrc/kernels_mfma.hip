@@ -764,13 +764,25 @@ __global__ __launch_bounds__(DMA ? 256 * KS + 64 * kLoadWaves : 256 * KS) void p
                 if (a.k_new != nullptr && ts + KT > new0) {
                     const char *nb = reinterpret_cast<const char *>((is_v ? a.v_new : a.k_new) +
                                                                     ((size_t)s * R * a.Hkv + kvh) * D);
+                    const size_t rs = (size_t)a.Hkv * 2 * D;          // bytes from one new row to the next
+                    if (ts >= new0 && ts + KT <= L) {
+                        // the whole sub-tile is new rows: one base, as for a page
+                        const char *nt = nb + (size_t)(ts - new0) * rs;
+#pragma unroll
+                        for (int j = 0; j < KT / 4 / LPS; ++j) {
+                            const int r = prow0 + 4 * j + (lane >> 4);
+                            const int piece = (lane & 15) ^ (is_v ? 2 * (r & 7) : (r & 15));
+                            load_to_lds<NTL>(nt + r * rs + 16 * piece, sub + (prow0 + 4 * j) * 2 * D);
+                        }
+                        return;
+                    }
 #pragma unroll
                     for (int j = 0; j < KT / 4 / LPS; ++j) {
                         const int r = prow0 + 4 * j + (lane >> 4);
                         const int piece = (lane & 15) ^ (is_v ? 2 * (r & 7) : (r & 15));
                         const int key = ts + r;
                         const char *src = key >= new0
-                                              ? nb + (size_t)min(key - new0, R - 1) * a.Hkv * 2 * D + 16 * piece
+                                              ? nb + (size_t)min(key - new0, R - 1) * rs + 16 * piece
                                               : base + r * 2 * D + 16 * piece;
                         load_to_lds<NTL>(src, sub + (prow0 + 4 * j) * 2 * D);
                     }
