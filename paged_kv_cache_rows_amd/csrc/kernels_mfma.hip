@@ -754,6 +754,22 @@ __global__ __launch_bounds__(DMA ? 256 * KS + 64 * kLoadWaves : 256 * KS) void p
             // k_new / v_new [S][R][Hkv][D]; a key past the stream (tail of the last sub-tile,
             // masked) rereads row R - 1
             const int new0 = L - R;
+            // Per-lane part of a load's source offset: the lane's row within its group of 4
+            // (lane >> 4) and its permuted piece.  prow0 is a multiple of 16, so the
+            // permutation of load j repeats every 4 loads for K (row & 15) and every 2 for V
+            // (2 (row & 7)); a load's address is then a wave-uniform base plus one of these,
+            // about 2 VALU instructions per load instead of 7.  Split calls (which the loads
+            // bound) use them: the verify window, warm 37.6-37.8 -> 35.5-35.8 us, cold part
+            // kernel 33.9-34.4 -> 32.9-33.5 us; prompt chunks, which the math bounds, measured
+            // 1 us slower per prompt with them and keep the per-load form.
+            static_assert((KT / LPS) % 16 == 0, "rows of a loading wave start at a multiple of 16");
+            int pk_off[4], pv_off[2];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) pk_off[q] = 16 * ((lane & 15) ^ ((4 * q + (lane >> 4)) & 15));
+#pragma unroll
+            for (int q = 0; q < 2; ++q) pv_off[q] = 16 * ((lane & 15) ^ (2 * ((4 * q + (lane >> 4)) & 7)));
+            const int lrow = (lane >> 4) * 2 * D;
+            auto poff = [&](int j, bool is_v) { return is_v ? pv_off[j & 1] : pk_off[j & 3]; };
             auto pload = [&](int it, const uint16_t *pages, char *sub, bool is_v) {
                 const int ts = kt_first + (it * KS + psub) * KT;
                 if (ts >= kend) return;
@@ -767,12 +783,21 @@ __global__ __launch_bounds__(DMA ? 256 * KS + 64 * kLoadWaves : 256 * KS) void p
                     const size_t rs = (size_t)a.Hkv * 2 * D;          // bytes from one new row to the next
                     if (ts >= new0 && ts + KT <= L) {
                         // the whole sub-tile is new rows: one base, as for a page
-                        const char *nt = nb + (size_t)(ts - new0) * rs;
+                        if constexpr (DEEP) {
+                            const char *nt = nb + (size_t)(ts - new0 + prow0) * rs;
+                            const int lnew = (lane >> 4) * (int)rs;
 #pragma unroll
-                        for (int j = 0; j < KT / 4 / LPS; ++j) {
-                            const int r = prow0 + 4 * j + (lane >> 4);
-                            const int piece = (lane & 15) ^ (is_v ? 2 * (r & 7) : (r & 15));
-                            load_to_lds<NTL>(nt + r * rs + 16 * piece, sub + (prow0 + 4 * j) * 2 * D);
+                            for (int j = 0; j < KT / 4 / LPS; ++j)
+                                load_to_lds<NTL>(nt + (size_t)(4 * j) * rs + (lnew + poff(j, is_v)),
+                                                 sub + (prow0 + 4 * j) * 2 * D);
+                        } else {
+                            const char *nt = nb + (size_t)(ts - new0) * rs;
+#pragma unroll
+                            for (int j = 0; j < KT / 4 / LPS; ++j) {
+                                const int r = prow0 + 4 * j + (lane >> 4);
+                                const int piece = (lane & 15) ^ (is_v ? 2 * (r & 7) : (r & 15));
+                                load_to_lds<NTL>(nt + r * rs + 16 * piece, sub + (prow0 + 4 * j) * 2 * D);
+                            }
                         }
                         return;
                     }
@@ -788,11 +813,18 @@ __global__ __launch_bounds__(DMA ? 256 * KS + 64 * kLoadWaves : 256 * KS) void p
                     }
                     return;
                 }
+                if constexpr (DEEP) {
+                    const char *bp = base + prow0 * 2 * D;
 #pragma unroll
-                for (int j = 0; j < KT / 4 / LPS; ++j) {
-                    const int r = prow0 + 4 * j + (lane >> 4);
-                    const int piece = (lane & 15) ^ (is_v ? 2 * (r & 7) : (r & 15));
-                    load_to_lds<NTL>(base + r * 2 * D + 16 * piece, sub + (prow0 + 4 * j) * 2 * D);
+                    for (int j = 0; j < KT / 4 / LPS; ++j)
+                        load_to_lds<NTL>(bp + 4 * j * 2 * D + (lrow + poff(j, is_v)), sub + (prow0 + 4 * j) * 2 * D);
+                } else {
+#pragma unroll
+                    for (int j = 0; j < KT / 4 / LPS; ++j) {
+                        const int r = prow0 + 4 * j + (lane >> 4);
+                        const int piece = (lane & 15) ^ (is_v ? 2 * (r & 7) : (r & 15));
+                        load_to_lds<NTL>(base + r * 2 * D + 16 * piece, sub + (prow0 + 4 * j) * 2 * D);
+                    }
                 }
             };
             auto pfix = [&](int it, char *sub) {
