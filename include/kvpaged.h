@@ -276,9 +276,11 @@ kv_status paged_attn_prefill(const kv_pool *pool, const kv_layout *lay, const kv
 
 /* kv_rows_put of a prompt chunk's R rows followed by paged_attn_prefill (TensorFold PR #1620,
  * opening description, Writes and Reads bullets), in one launch where the call runs the MFMA
- * kernel at head_dim 128 over pages of a multiple of 64 positions (R times the group at least
- * 16: every prompt chunk of that shape), or where R = 1 on the VALU kernel; otherwise as a
- * row-write launch followed by the attention on the same stream.  In the one-launch form each
+ * kernel that loads whole 64-key tiles straight into LDS (R times the group at least 16,
+ * head_dim 128, pages of a multiple of 64 positions, and a workgroup's keys within the 160
+ * table entries it caches: every prompt chunk of up to about 10,000 keys over pages of 64, or
+ * 80,000 over pages of 512), or where R = 1 on the VALU kernel; otherwise as a row-write
+ * launch followed by the attention on the same stream.  In the one-launch form each
  * new row is written into its page slot by one workgroup, and the attention reads the call's
  * own rows from k_new and v_new rather than from those slots.  k_new, v_new: device bf16
  * [S][R][Hkv][D] (16-byte aligned, caller-owned), row r of stream s written at position
