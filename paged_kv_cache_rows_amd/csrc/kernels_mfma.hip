@@ -841,11 +841,13 @@ __global__ __launch_bounds__(DMA ? 256 * KS + 64 * kLoadWaves : 256 * KS) void p
                 // Four buffers per operand: in step j the computing waves read K(j + 1) and
                 // V(j), while K(j + 4) and V(j + 3) are issued into the buffers of K(j) and
                 // V(j - 1), and the wait is for K(j + 2) and V(j + 1), issued two steps before:
-                // the 4 newest groups of 4 loads of this wave may stay in flight (vmcnt 16) when
-                // all of them were issued in full, else every load is waited for.
+                // the 4 newest groups of NL loads of this wave may stay in flight when all of them
+                // were issued in full, else every load is waited for (with four loading waves
+                // NL is 4; two, which issue the same loads at the same cold time, would make it 8).
                 auto kb = [&](int i) { return reinterpret_cast<char *>(k_lds_all[i & (NBUF - 1)][psub]); };
                 auto vb = [&](int i) { return reinterpret_cast<char *>(vt_lds_all[i & (NBUF - 1)][psub]); };
-                static_assert(KT / 4 / LPS == 4, "4 loads per wave, operand and step");
+                constexpr int NL = KT / 4 / LPS;   // loads per wave, operand and step
+                static_assert(6 * NL < 64, "vmcnt range");
                 const bool ahead = nsteps >= 5;
                 pload(0, a.k_pages, kb(0), false);
                 pload(1, a.k_pages, kb(1), false);
@@ -854,9 +856,9 @@ __global__ __launch_bounds__(DMA ? 256 * KS + 64 * kLoadWaves : 256 * KS) void p
                 pload(1, a.v_pages, vb(1), true);
                 pload(3, a.k_pages, kb(3), false);
                 pload(2, a.v_pages, vb(2), true);
-                if (ahead) wait_vmcnt<24>(); else wait_vmem();    // K(0)
+                if (ahead) wait_vmcnt<6 * NL>(); else wait_vmem();    // K(0)
                 loader_barrier();
-                if (ahead) wait_vmcnt<16>(); else wait_vmem();    // K(1), V(0)
+                if (ahead) wait_vmcnt<4 * NL>(); else wait_vmem();    // K(1), V(0)
                 pfix(0, vb(0));
                 loader_barrier();   // the computing waves' scores of step 0
                 for (int it = 0; it < nsteps; it += 2) {
@@ -865,7 +867,7 @@ __global__ __launch_bounds__(DMA ? 256 * KS + 64 * kLoadWaves : 256 * KS) void p
                         const int j = it + h;
                         pload(j + 4, a.k_pages, kb(j + 4), false);
                         pload(j + 3, a.v_pages, vb(j + 3), true);
-                        if (j + 4 <= nsteps - 2) wait_vmcnt<16>(); else wait_vmem();   // K(j + 2), V(j + 1)
+                        if (j + 4 <= nsteps - 2) wait_vmcnt<4 * NL>(); else wait_vmem();   // K(j + 2), V(j + 1)
                         pfix(j + 1, vb(j + 1));
                         loader_barrier();
                     }
