@@ -86,6 +86,12 @@ bool mfma_supported(int D, int G, int R) {
     return (D == 128 || D == 256 || D == 512) && (G == 4 || G == 8 || G == 12 || G == 16) && R >= 1 && R * G >= 16;
 }
 
+// d 512 calls of 16 to 32 query vectors per KV head over pages of at least 32 keys (a verify
+// window of a few rows) run the channel-split kernel (part_narrow_kernel below); its plan counts
+// chunks in units of this many 32-key tiles.
+constexpr int kNarrowTiles = 3;
+constexpr bool narrow_shape(int D, int NQ, int P) { return D == 512 && NQ >= 16 && NQ <= 32 && P >= 32; }
+
 // Query-column blocks per wave, query tiles and chunk length of one call.  Everything here is
 // a function of the call's shape (never of page ids or device lengths), so the chunk
 // boundaries, and with them the result, do not depend on where pages live.
@@ -108,6 +114,22 @@ MfmaPlan mfma_plan(int D, int G, int R, int S, int Hkv, int P, int max_seq_len, 
     // enough query tiles to fill the CUs: one split per tile, whose output is then written
     // directly (partials and their merge cost far more than their bytes: a 512-row prompt
     // chunk over 2048 keys takes 53 us with 4 splits and a merge, 38 us with one)
+    // The channel-split kernel at d 512 (not for direct calls, which fill the GPU with tiles):
+    // chunks of whole batches, as few batches per workgroup as keep the call in one round of one
+    // workgroup per CU, within the table entries a workgroup caches.
+    if (groups < 256 && narrow_shape(D, nq, P)) {
+        const int64_t unit = (int64_t)kNarrowTiles * kt;
+        const int64_t cap = ((int64_t)(MfmaGeom<128>::TC - 2) * P - kt) / kt * kt;
+        int64_t c = unit;
+        for (;;) {
+            int64_t ns = (max_seq_len + c - 1) / c;
+            if (window > 0) ns = std::min(ns, (span + c - 1) / c + 1);
+            if (groups * ns <= 256 || c + unit > cap) break;
+            c += unit;
+        }
+        p.chunk = (int)c;
+        return p;
+    }
     if (groups >= 256) {
         p.direct = true;
         p.chunk = (span + kt - 1) / kt * kt;     // bounds the keys of one tile
@@ -1061,6 +1083,359 @@ __global__ __launch_bounds__(DMA ? 256 * KS + 64 * kLoadWaves : 256 * KS) void p
     }
 }
 
+// ---------------------------------------------------------------------------------------------
+// d 512 with at most 32 query vectors per KV head (verify windows of a few rows): the
+// channel-split kernel.  TensorFold PR #1620, per-tile follow-up (the head-dim-512 layer's
+// verify rows, timed alone with a cold L2).
+//
+// With 16 or 32 query vectors the tile kernel above leaves two of its four waves idle, and each
+// live wave takes both products over all 512 channels at one wave per SIMD, a chain of 64 MFMAs
+// per 32-key tile, each waiting on its own LDS read.  Here wave w owns channels
+// 128 w .. 128 w + 127 of the queries, keys and values:
+//  * S^T = K Q^T over the wave's channels, with K loaded from memory straight into the A-operand
+//    registers (lane: key 16 nb + col, 8 channels of its lane group), no LDS;
+//  * the four waves' partial scores are added through LDS in one fixed order, so every wave
+//    holds the same full scores, runs the same online softmax on them and gets the same bits;
+//  * O^T += V^T P^T for the wave's 128 output channels: each wave loads its own 256-byte slice
+//    of the tile's V rows straight into LDS (rows of 256 bytes, 16-byte pieces permuted as in the
+//    d 128 direct-to-LDS layout) and reads V^T back with transposing reads.
+// Tiles stream through a ring of three buffers, the next one in flight while one is computed.
+// Pages hold at least 32 keys, so a tile lies in at most two pages: one division and two cached
+// table entries per tile.  MODE 0: P % 32 == 0, one page per tile.
+// Measured on the 4-row verify at 9,000 keys over pages of 37 (188 workgroups, one per CU):
+// cold part kernel 26.9-27.2 us against 27.4-27.8 for the tile kernel, warm 21.0-21.6 against
+// 24.2-25.4.  Each workgroup streams 192 KB of K/V, and a plain read of the same bytes with the
+// same grid and bytes per workgroup takes 17.4-18.1 us cold: at this shape the CU's streaming
+// rate (about 21 GB/s per CU with every workgroup loading), not the math, bounds the call.
+
+template <int QB, int MODE>
+__global__ __launch_bounds__(256) void part_narrow_kernel(const PartArgs a) {
+    constexpr int D = 512, KT = 32, CW = 128;   // keys per tile, channels per wave
+    constexpr int NKB = CW / 32;                // QK k-steps per wave
+    constexpr int NCB = CW / 16;                // PV output blocks per wave
+    constexpr int NBT = kNarrowTiles;
+    constexpr int TC = kTableCache;
+    constexpr int NF = 2 * QB;                  // score fragments per lane (query x key blocks)
+    __shared__ __attribute__((aligned(16))) char v_lds[NBT][4][KT * CW * 2];
+    __shared__ __attribute__((aligned(16))) f32x4_t xch[2][4][NF][64];
+    __shared__ int32_t t_lds[TC];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int col = lane & 15, grp = lane >> 4;
+    // work items (stream, KV head, split) in XCD order, as in the tile kernel
+    const int item = (blockIdx.x & 7) * a.per_xcd + (blockIdx.x >> 3);
+    if (item >= a.S * a.Hkv * a.n_splits) return;
+    const int split = item % a.n_splits;
+    const int kvh = (item / a.n_splits) % a.Hkv;
+    const int s = item / (a.n_splits * a.Hkv);
+    const int R = a.R, W = a.window, CH = a.chunk;
+    const int G = a.Hq / a.Hkv;
+    const int NQ = R * G;
+    const int32_t *trow = a.table + (size_t)s * a.stride;
+
+    // queries of this wave's channels as the B operand (column 16 b + col, channels
+    // 128 wave + 32 kb + 8 grp .. + 8), issued together with the length and, for a full layer
+    // whose table fits the cache, the table entries
+    const bool whole = whole_table(MODE, a.ring_pages, a.stride);
+    const int Lv = load_uniform_i32(a.seq_len + s);
+    bool col_ok[QB];
+    int rq[QB], hq[QB];
+    uint32_t anc[QB];
+    bf16x8_t qf[QB][NKB];
+#pragma unroll
+    for (int b = 0; b < QB; ++b) {
+        const int vq = 16 * b + col;
+        col_ok[b] = vq < NQ;
+        rq[b] = col_ok[b] ? vq / G : 0;
+        hq[b] = kvh * G + (col_ok[b] ? vq % G : 0);
+        anc[b] = a.tree ? a.tree[s * R + rq[b]] : 0xFFFFFFFFu;
+        const uint16_t *qrow = a.q + ((size_t)(s * R + rq[b]) * a.Hq + hq[b]) * D + CW * wave + 8 * grp;
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+            u32x4 x = *reinterpret_cast<const u32x4 *>(qrow + 32 * kb);
+            if (!col_ok[b]) x = u32x4{0, 0, 0, 0};
+            qf[b][kb] = __builtin_bit_cast(bf16x8_t, x);
+        }
+    }
+    constexpr int TPT = (TC + 255) / 256;
+    int tv[TPT];
+    if (whole) {
+#pragma unroll
+        for (int k = 0; k < TPT; ++k) {
+            const int i = tid + k * 256;
+            tv[k] = i < a.stride ? trow[i] : -1;
+        }
+    }
+    const int L = kernel_len(__builtin_amdgcn_readfirstlane(Lv), a.max_len);
+    if (whole) {
+#pragma unroll
+        for (int k = 0; k < TPT; ++k) {
+            const int i = tid + k * 256;
+            if (i < TC) t_lds[i] = ((unsigned)tv[k] < (unsigned)a.num_pages) ? tv[k] : -1;
+        }
+    }
+    const int p_first = L - R, p_last = L - 1;
+    const KeyRange keys = mfma_keys(L, R, W, CH, split, false, 0, R - 1);
+    const int kbeg = keys.kbeg, kend = keys.kend;
+    if (kbeg >= kend) return;   // no row sees this chunk: nothing to merge
+    const int lo_full = W > 0 ? p_last - W + 1 : 0;
+    const int hi_full = a.tree ? min(p_first, L - R - 1) : p_first;
+    const int win0 = L - R;
+    int p_col[QB], lo_col[QB];
+#pragma unroll
+    for (int b = 0; b < QB; ++b) {
+        p_col[b] = L - R + rq[b];
+        lo_col[b] = W > 0 ? p_col[b] - W + 1 : 0;
+    }
+    const int P = a.P;
+    const int kt_first = (kbeg / KT) * KT;
+    const int nt = (kend - kt_first + KT - 1) / KT;
+    const int idx0 = whole ? 0 : kt_first / P;
+    if (!whole) {
+        for (int i = tid; i < TC; i += 256) {
+            int idx = idx0 + i;
+            if (a.ring_pages) idx %= a.ring_pages;
+            int pg = -1;
+            if (idx < a.stride) pg = trow[idx];
+            t_lds[i] = ((unsigned)pg < (unsigned)a.num_pages) ? pg : -1;
+        }
+    }
+    lds_fence();
+
+    const size_t page_elems = (size_t)a.Hkv * P * D;
+    const size_t head_off = (size_t)kvh * P * D;
+    // Issue the loads of tile t (absolute start kt_first + 32 t) into K register set kr and V
+    // buffer vb: rows r < sp lie in page pa at offset off0 + r, the others in page pb at r - sp.
+    // 8 K loads (this lane's two key rows x four k-steps), then 8 V loads into LDS.
+    auto issue = [&](int t, u32x4 (&kr)[2][NKB], char *vb) {
+        const int tb = kt_first + KT * t;
+        const int idx = tb / P;
+        const int off0 = tb - idx * P;
+        const int pga = __builtin_amdgcn_readfirstlane(cached_page<TC>(t_lds, idx - idx0));
+        const int pgb = MODE == 0 ? pga : __builtin_amdgcn_readfirstlane(cached_page<TC>(t_lds, idx + 1 - idx0));
+        const size_t ea = (size_t)pga * page_elems + head_off + (size_t)off0 * D;
+        const size_t eb = (size_t)pgb * page_elems + head_off;
+        const int sp = MODE == 0 ? KT : P - off0;
+        auto row = [&](int r) { return r < sp ? ea + (size_t)r * D : eb + (size_t)(r - sp) * D; };
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) {
+            const uint16_t *kp = a.k_pages + row(16 * nb + col) + CW * wave + 8 * grp;
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) kr[nb][kb] = *reinterpret_cast<const u32x4 *>(kp + 32 * kb);
+        }
+#pragma unroll
+        for (int j = 0; j < KT / 4; ++j) {
+            const int r = 4 * j + grp;
+            const int piece = (lane & 15) ^ (2 * (r & 7));
+            const char *src = reinterpret_cast<const char *>(a.v_pages + row(r) + CW * wave) + 16 * piece;
+            load_to_lds<false>(src, vb + 4 * j * 2 * CW);
+        }
+    };
+
+    f32x4_t o[QB][NCB];
+    float m_run[QB], l_run[QB];
+#pragma unroll
+    for (int b = 0; b < QB; ++b) {
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) o[b][cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        m_run[b] = -INFINITY;
+        l_run[b] = 0.f;
+    }
+    const float c2 = a.scale_log2;
+    const float slack = fminf(8.0f / c2, 3.0e38f);
+    const bf16x8_t ones8 = __builtin_bit_cast(bf16x8_t, u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
+    // V^T operand reads: rows 4 grp + (col >> 2) (+ 16), channels 16 cb + 4 (col & 3) of the
+    // wave's slice (the d 128 direct-to-LDS layout)
+    int v_rd[NCB];
+    {
+        const int vr = 4 * grp + (col >> 2);
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) v_rd[cb] = vr * 2 * CW + 32 * (cb ^ (vr & 7)) + 8 * (col & 3);
+    }
+
+    // one tile: scores over the wave's channels, their sum over the waves, mask, online softmax,
+    // PV into the wave's output channels
+    auto compute = [&](int t, const u32x4 (&kr)[2][NKB], const char *vb) {
+        const int tb = kt_first + KT * t;
+        f32x4_t sacc[QB][2];
+#pragma unroll
+        for (int b = 0; b < QB; ++b)
+#pragma unroll
+            for (int nb = 0; nb < 2; ++nb) {
+                sacc[b][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kb = 0; kb < NKB; ++kb)
+                    sacc[b][nb] = mfma16(__builtin_bit_cast(bf16x8_t, kr[nb][kb]), qf[b][kb], sacc[b][nb]);
+            }
+        const int par = t & 1;
+#pragma unroll
+        for (int b = 0; b < QB; ++b)
+#pragma unroll
+            for (int nb = 0; nb < 2; ++nb) xch[par][wave][2 * b + nb][lane] = sacc[b][nb];
+        // the waves' partial scores are in LDS (V loads stay in flight); with two exchange
+        // buffers a wave writes buffer par again only after the next barrier, which every wave
+        // passes after its reads of this one
+        loader_barrier();
+#pragma unroll
+        for (int b = 0; b < QB; ++b)
+#pragma unroll
+            for (int nb = 0; nb < 2; ++nb) {
+                const f32x4_t x0 = xch[par][0][2 * b + nb][lane], x1 = xch[par][1][2 * b + nb][lane];
+                const f32x4_t x2 = xch[par][2][2 * b + nb][lane], x3 = xch[par][3][2 * b + nb][lane];
+                sacc[b][nb] = (x0 + x1) + (x2 + x3);
+            }
+        const bool full = tb >= kbeg && tb + KT <= kend && tb + KT - 1 <= hi_full && tb >= lo_full;
+        bf16x8_t pf[QB];
+#pragma unroll
+        for (int b = 0; b < QB; ++b) {
+            float tmax = -INFINITY;
+            if (full) {
+#pragma unroll
+                for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) tmax = fmaxf(tmax, sacc[b][nb][r]);
+            } else {
+#pragma unroll
+                for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int j = tb + 16 * nb + 4 * grp + r;
+                        const int tw = j - win0;
+                        const bool vis = col_ok[b] & (j >= kbeg) & (j < kend) & (j <= p_col[b]) & (j >= lo_col[b]) &
+                                         ((tw < 0) | (((anc[b] >> (tw & 31)) & 1u) != 0));
+                        const float x = vis ? sacc[b][nb][r] : -INFINITY;
+                        sacc[b][nb][r] = x;
+                        tmax = fmaxf(tmax, x);
+                    }
+            }
+            if (__builtin_amdgcn_ballot_w64(tmax > m_run[b] + slack)) {
+                tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+                tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+                const float m_new = fmaxf(m_run[b], tmax);
+                const float mc_new = (m_new == -INFINITY) ? 0.f : m_new * c2;
+                const float alpha = fast_exp2(m_run[b] * c2 - mc_new);
+                m_run[b] = m_new;
+                l_run[b] *= alpha;
+                if (alpha != 1.f) {
+#pragma unroll
+                    for (int cb = 0; cb < NCB; ++cb) o[b][cb] *= alpha;
+                }
+            }
+            const float mc = (m_run[b] == -INFINITY) ? 0.f : m_run[b] * c2;
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) pf[b][4 * hh + r] = (__bf16)fast_exp2(__builtin_fmaf(sacc[b][hh][r], c2, -mc));
+            const f32x4_t ls = mfma16(ones8, pf[b], f32x4_t{0.f, 0.f, 0.f, 0.f});
+            l_run[b] += ls[0];
+        }
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) {
+            const v4i16_t lo = lds_read_tr16(vb + v_rd[cb]);
+            const v4i16_t hi = lds_read_tr16(vb + v_rd[cb] + 16 * 2 * CW);
+            const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
+            const bf16x8_t vv = __builtin_bit_cast(bf16x8_t, u32x4{l2.x, l2.y, h2.x, h2.y});
+#pragma unroll
+            for (int b = 0; b < QB; ++b) o[b][cb] = mfma16(vv, pf[b], o[b][cb]);
+        }
+    };
+    // zero the rows of V buffer vb (tile t, loaded by this lane) outside [kbeg, kend): unused
+    // slots may hold NaN, which a zero weight would not cancel
+    auto vfix = [&](int t, char *vb) {
+        const int tb = kt_first + KT * t;
+        if (tb >= kbeg && tb + KT <= kend) return;
+#pragma unroll
+        for (int j = 0; j < KT / 4; ++j) {
+            const int key = tb + 4 * j + grp;
+            if (key < kbeg || key >= kend) *reinterpret_cast<u32x4 *>(vb + 4 * j * 2 * CW + 16 * lane) = u32x4{0u, 0u, 0u, 0u};
+        }
+    };
+
+    // A ring of three tiles (K register sets k0..k2, V buffers vb0..vb2; tile t in set t mod 3).
+    // Tile t + 2 is issued right after tile t is computed, into the set tile t - 1 used, so one
+    // tile streams in while one is computed.  A wave whose loads fill the CU's memory queue
+    // stalls at issue until data returns, and the score exchange makes every wave wait for the
+    // slowest one: issuing further ahead only moves the compute behind the stream (tile t + 2
+    // issued before tile t is computed: cold part kernel of the 4-row verify at 9,000 keys
+    // 26.9-27.2 us).  The main loop issues only tiles inside the chunk and waits for a fixed
+    // count (the 16 loads of the next tile stay in flight); the tail (at most four tiles)
+    // spells out its waits.
+    u32x4 k0[2][NKB], k1[2][NKB], k2[2][NKB];
+    char *const vb0 = v_lds[0][wave], *const vb1 = v_lds[1][wave], *const vb2 = v_lds[2][wave];
+    auto fence = [] { asm volatile("" ::: "memory"); };
+    issue(0, k0, vb0);
+    fence();
+    issue(min(1, nt - 1), k1, vb1);   // a chunk of one tile rereads it
+    fence();
+    int t = 0;
+    for (; t + 5 <= nt; t += 3) {
+        wait_vmcnt<16>();
+        fence();
+        vfix(t, vb0);
+        compute(t, k0, vb0);
+        issue(t + 2, k2, vb2);
+        fence();
+        wait_vmcnt<16>();
+        fence();
+        vfix(t + 1, vb1);
+        compute(t + 1, k1, vb1);
+        issue(t + 3, k0, vb0);
+        fence();
+        wait_vmcnt<16>();
+        fence();
+        vfix(t + 2, vb2);
+        compute(t + 2, k2, vb2);
+        issue(t + 4, k1, vb1);
+        fence();
+    }
+    // tail: tiles t .. nt - 1 (1 to 4 of them); t and t + 1 (or t again) are issued
+    const int rem = nt - t;
+    wait_vmcnt<16>();
+    fence();
+    vfix(t, vb0);
+    compute(t, k0, vb0);
+    if (rem >= 3) issue(t + 2, k2, vb2);
+    fence();
+    if (rem >= 2) {
+        if (rem >= 3) wait_vmcnt<16>(); else wait_vmem();
+        fence();
+        vfix(t + 1, vb1);
+        compute(t + 1, k1, vb1);
+    }
+    if (rem >= 4) issue(t + 3, k0, vb0);
+    fence();
+    if (rem >= 3) {
+        if (rem >= 4) wait_vmcnt<16>(); else wait_vmem();
+        fence();
+        vfix(t + 2, vb2);
+        compute(t + 2, k2, vb2);
+    }
+    if (rem >= 4) {
+        wait_vmem();
+        fence();
+        vfix(t + 3, vb0);
+        compute(t + 3, k0, vb0);
+    }
+    wait_vmem();   // a one-tile chunk's reread
+    fence();
+
+    // partials: this wave's 128 channels of each column, (m, l) from wave 0
+#pragma unroll
+    for (int b = 0; b < QB; ++b) {
+        if (!col_ok[b]) continue;
+        const size_t slot = ((size_t)(s * R + rq[b]) * a.Hq + hq[b]) * a.n_splits + split;
+        float *dst = a.ws_acc + slot * D + CW * wave + 4 * grp;
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb)
+            *reinterpret_cast<float4 *>(dst + 16 * cb) = make_float4(o[b][cb][0], o[b][cb][1], o[b][cb][2], o[b][cb][3]);
+        if (wave == 0 && grp == 0) {
+            const float m2 = m_run[b] == -INFINITY ? -INFINITY : m_run[b] * c2;
+            *reinterpret_cast<float2 *>(a.ws_ml + slot * 2) = make_float2(m2, l_run[b]);
+        }
+    }
+}
+
 template <int D, int G, int QW, int KS, bool NTL>
 static hipError_t launch_dgq(const PartArgs &a, hipStream_t st) {
     using Geo = MfmaGeom<D>;
@@ -1103,6 +1478,19 @@ hipError_t launch_part_mfma(int D, int G, const MfmaPlan &p, const PartArgs &arg
     if (items > (int64_t)1 << 30) return hipErrorInvalidValue;
     a.per_xcd = (int)((items + 7) / 8);
     if (p.qw != 1 || p.ks != (D == 128 ? 2 : 1)) return hipErrorInvalidValue;
+    if (!p.direct && narrow_shape(D, a.R * G, a.P) && table_mode(a.P, a.chunk, 32, 32) != 2) {
+        if (p.tiles != 1) return hipErrorInvalidValue;
+        const dim3 grid(8 * a.per_xcd);
+        const bool one = a.R * G <= 16;
+        if (a.P % 32 == 0) {
+            if (one) hipLaunchKernelGGL((part_narrow_kernel<1, 0>), grid, dim3(256), 0, st, a);
+            else hipLaunchKernelGGL((part_narrow_kernel<2, 0>), grid, dim3(256), 0, st, a);
+        } else {
+            if (one) hipLaunchKernelGGL((part_narrow_kernel<1, 1>), grid, dim3(256), 0, st, a);
+            else hipLaunchKernelGGL((part_narrow_kernel<2, 1>), grid, dim3(256), 0, st, a);
+        }
+        return hipGetLastError();
+    }
     if (D == 128 && G == 4) return launch_dg<128, 4, 2>(a, st);
     if (D == 128 && G == 8) return launch_dg<128, 8, 2>(a, st);
     if (D == 128 && G == 12) return launch_dg<128, 12, 2>(a, st);
