@@ -188,8 +188,9 @@ bool mfma_supported(int D, int G, int R);
 int valu_batch_keys(int D);
 int valu_rows_per_load(int D);
 int valu_table_mode(int D, int P, int chunk);
-// VALU waves per workgroup and load slots per wave (RPI rows each) for NQ query vectors.
-void valu_load_shape(int NQ, int *waves, int *slots_per_wave);
+// VALU waves per workgroup and load slots per wave (RPI rows each) for NQ query vectors at head
+// dim D.
+void valu_load_shape(int D, int NQ, int *waves, int *slots_per_wave);
 int mfma_tile_keys(int D);
 int mfma_table_mode(int D, int P, int chunk);
 

@@ -138,11 +138,14 @@ struct BatchLoader {
     }
 };
 
-// Query vectors per wave (VW) and waves per workgroup (NW = NQ / VW).
-template <int NQ>
-constexpr int valu_vw() { return NQ % 2 == 0 && NQ <= 8 ? 2 : 4; }
-template <int NQ>
-constexpr int valu_waves() { return NQ / valu_vw<NQ>(); }
+// Query vectors per wave (VW) and waves per workgroup (NW = NQ / VW).  At d 512 with 8 vectors,
+// one per wave (8 waves, two per SIMD): a d 512 decode is a short chain of dependent LDS reads
+// and dot2s per batch, which a second wave on the SIMD hides (2,048-key decode over pages of
+// 37, cold part kernel 11.9 -> 11.3 us; bytes unchanged).
+template <int D, int NQ>
+constexpr int valu_vw() { return D == 512 && NQ == 8 ? 1 : NQ % 2 == 0 && NQ <= 8 ? 2 : 4; }
+template <int D, int NQ>
+constexpr int valu_waves() { return NQ / valu_vw<D, NQ>(); }
 
 // Load modes, fixed per launch from P (table_mode over batches of NB keys): 0 when P is a
 // multiple of the batch, 1 when rows straddle pages but the chunk's table entries fit the LDS
@@ -157,13 +160,13 @@ int valu_mode(int P, int chunk) {
 // lookups of MODEs 1 and 2 need a few more registers than that and would spill, so those modes
 // have no occupancy floor.
 template <int D, int G, int NQ, int MODE>
-__global__ __launch_bounds__(64 * valu_waves<NQ>()) __attribute__((amdgpu_waves_per_eu(D == 128 && NQ == 8 && MODE == 0 ? 4 : 1, 8))) void part_valu_kernel(const PartArgs a) {
+__global__ __launch_bounds__(64 * (valu_waves<D, NQ>())) __attribute__((amdgpu_waves_per_eu(D == 128 && NQ == 8 && MODE == 0 ? 4 : 1, 8))) void part_valu_kernel(const PartArgs a) {
     using Geo = ValuGeom<D>;
     constexpr int LPR = Geo::LPR, RPI = Geo::RPI, NB = Geo::NB, QL = Geo::QL, SEG = Geo::SEG;
     constexpr int RS = Geo::RS, TC = Geo::TC;
     constexpr int R = NQ / G;
-    constexpr int VW = valu_vw<NQ>();                   // query vectors per wave
-    constexpr int NW = valu_waves<NQ>();
+    constexpr int VW = valu_vw<D, NQ>();                // query vectors per wave
+    constexpr int NW = valu_waves<D, NQ>();
     using Loader = BatchLoader<D, NW>;
     constexpr int NS = Loader::NS;
     constexpr int PRS = 2 * D + 8;                      // V pair-row stride (bf16 elements): 528 bytes at
@@ -415,8 +418,10 @@ __global__ __launch_bounds__(64 * valu_waves<NQ>()) __attribute__((amdgpu_waves_
             if (writer) {
                 if constexpr (VW == 4)
                     *reinterpret_cast<u32x4 *>(p_mine + pid * VW) = u32x4{w[0], w[1], w[2], w[3]};
-                else
+                else if constexpr (VW == 2)
                     *reinterpret_cast<uint2 *>(p_mine + pid * VW) = make_uint2(w[0], w[1]);
+                else
+                    p_mine[pid] = w[0];
             }
         }
         wave_lds_fence();
@@ -433,9 +438,11 @@ __global__ __launch_bounds__(64 * valu_waves<NQ>()) __attribute__((amdgpu_waves_
             if constexpr (VW == 4) {
                 const u32x4 pp = *reinterpret_cast<const u32x4 *>(p_mine + pr * VW);
                 pw[0] = pp.x; pw[1] = pp.y; pw[2] = pp.z; pw[3] = pp.w;
-            } else {
+            } else if constexpr (VW == 2) {
                 const uint2 pp = *reinterpret_cast<const uint2 *>(p_mine + pr * VW);
                 pw[0] = pp.x; pw[1] = pp.y;
+            } else {
+                pw[0] = p_mine[pr];
             }
 #pragma unroll
             for (int v = 0; v < VW; ++v)
@@ -483,16 +490,19 @@ int valu_rows_per_load(int D) {
 int valu_table_mode(int D, int P, int chunk) {
     return D == 512 ? valu_mode<512>(P, chunk) : D == 256 ? valu_mode<256>(P, chunk) : valu_mode<128>(P, chunk);
 }
-template <int NQ>
+template <int D, int NQ>
 static void load_shape(int *waves, int *slots) {
-    *waves = valu_waves<NQ>();
-    *slots = BatchLoader<128, valu_waves<NQ>()>::NS;
+    *waves = valu_waves<D, NQ>();
+    *slots = BatchLoader<D, valu_waves<D, NQ>()>::NS;
 }
-void valu_load_shape(int NQ, int *waves, int *slots_per_wave) {
+void valu_load_shape(int D, int NQ, int *waves, int *slots_per_wave) {
     *waves = *slots_per_wave = 0;
-    if (NQ == 4) load_shape<4>(waves, slots_per_wave);
-    if (NQ == 8) load_shape<8>(waves, slots_per_wave);
-    if (NQ == 12) load_shape<12>(waves, slots_per_wave);
+#define KVP_SHAPE(d)                                           \
+    if (D == d && NQ == 4) load_shape<d, 4>(waves, slots_per_wave);   \
+    if (D == d && NQ == 8) load_shape<d, 8>(waves, slots_per_wave);   \
+    if (D == d && NQ == 12) load_shape<d, 12>(waves, slots_per_wave);
+    KVP_SHAPE(128) KVP_SHAPE(256) KVP_SHAPE(512)
+#undef KVP_SHAPE
 }
 
 bool valu_supported(int D, int G, int NQ) {
@@ -505,7 +515,7 @@ bool valu_supported(int D, int G, int NQ) {
 
 template <int D, int G, int NQ>
 static hipError_t launch_one(const PartArgs &a, int S, hipStream_t st) {
-    constexpr int NW = valu_waves<NQ>();
+    constexpr int NW = valu_waves<D, NQ>();
     const dim3 grid(a.n_splits, a.Hkv, S);
     if (a.chunk % ValuGeom<D>::NB != 0) return hipErrorInvalidValue;
     switch (valu_mode<D>(a.P, a.chunk)) {

@@ -177,7 +177,7 @@ void check_valu(const Shape &c, const CallPlan &p, const Table &t, int Ldev) {
     const int stride = t.stride;
     const bool whole = whole_table(mode, c.ring, stride);
     int NW, NS;
-    valu_load_shape(c.R * c.G, &NW, &NS);
+    valu_load_shape(c.D, c.R * c.G, &NW, &NS);
     if (NW * NS < 16) report(c, L, "load slots do not cover a batch", NW, NS);
     if (mode == 1 && c.P < RPI) report(c, L, "per-row stepping with pages shorter than a load", c.P, RPI);
     const int lo = c.window > 0 ? std::max(0, L - c.R - c.window + 1) : 0;
