@@ -236,10 +236,11 @@ __device__ __forceinline__ f32x4_t mfma16(const bf16x8_t &a, const bf16x8_t &b, 
 
 // MODE 0: P % KT == 0 and the chunk's table entries cached in LDS (one lookup per tile);
 // MODE 1: entries cached, lookup per piece; MODE 2: lookup per piece in the global table.
-// NTL: K/V loads are nontemporal.  Used at d 128 where each key tile has one reader, so that
-// nothing is gained by keeping it in the caches (4 streams x 36k keys: 112 -> 96 us).  With
-// several query tiles per chunk the tiles reread it from L2, and at d 512 plain loads measured
-// faster (4-row verify at 9000 keys in pages of 37: 23.2 against 26.1 us), so those stay plain.
+// NTL: K/V loads are nontemporal.  Used wherever each key tile has one reader (one query tile
+// per chunk), so that nothing is gained by keeping it in the caches (4 streams x 36k keys at
+// d 128: 112 -> 96 us; 16/1 heads at d 512, 4 rows over pages of 512, cold part kernel at
+// 32,768 keys 41.0 -> 31.1 us, at 9,000 keys 28.1 -> 27.0 us).  With several query tiles per
+// chunk the tiles reread it from L2 and the loads stay plain.
 // KS: key sub-tiles per iteration.  With KS = 2 the workgroup has 8 waves: waves 4 g .. 4 g + 3
 // compute sub-tile g of each 2 KT-key step with an online softmax of their own, and the two
 // states are combined through LDS at the end, which halves the tile chain of a workgroup
@@ -1102,11 +1103,12 @@ __global__ __launch_bounds__(DMA ? 256 * KS + 64 * kLoadWaves : 256 * KS) void p
 // Tiles stream through a ring of three buffers, the next one in flight while one is computed.
 // Pages hold at least 32 keys, so a tile lies in at most two pages: one division and two cached
 // table entries per tile.  MODE 0: P % 32 == 0, one page per tile.
-// Measured on the 4-row verify at 9,000 keys over pages of 37 (188 workgroups, one per CU):
-// cold part kernel 26.9-27.2 us against 27.4-27.8 for the tile kernel, warm 21.0-21.6 against
-// 24.2-25.4.  Each workgroup streams 192 KB of K/V, and a plain read of the same bytes with the
-// same grid and bytes per workgroup takes 17.4-18.1 us cold: at this shape the CU's streaming
-// rate (about 21 GB/s per CU with every workgroup loading), not the math, bounds the call.
+// Measured on the 4-row verify at 9,000 keys over pages of 37 (188 workgroups, one per CU): cold
+// part kernel 20.9-21.0 us with nontemporal loads (26.9-27.2 with plain ones) against
+// 27.4-27.8 for the tile kernel.  Each workgroup streams 192 KB of K/V; a plain read of the same
+// bytes with the same grid and bytes per workgroup takes 17.4-18.1 us cold, so at this shape
+// the CU's streaming rate (about 21 GB/s per CU with every workgroup loading) bounds the call,
+// not the math.
 
 template <int QB, int MODE>
 __global__ __launch_bounds__(256) void part_narrow_kernel(const PartArgs a) {
@@ -1207,7 +1209,10 @@ __global__ __launch_bounds__(256) void part_narrow_kernel(const PartArgs a) {
     const size_t head_off = (size_t)kvh * P * D;
     // Issue the loads of tile t (absolute start kt_first + 32 t) into K register set kr and V
     // buffer vb: rows r < sp lie in page pa at offset off0 + r, the others in page pb at r - sp.
-    // 8 K loads (this lane's two key rows x four k-steps), then 8 V loads into LDS.
+    // 8 K loads (this lane's two key rows x four k-steps), then 8 V loads into LDS, all
+    // nontemporal: every K/V byte of the call is read once (4-row verify at 9,000 keys, cold
+    // part kernel 26.7-26.8 -> 20.9-21.0 us, whole call 32.0 -> 25.9 us; calls repeated back to
+    // back on the same keys, whose K/V could stay in the caches, 21.4 -> 25.2 us).
     auto issue = [&](int t, u32x4 (&kr)[2][NKB], char *vb) {
         const int tb = kt_first + KT * t;
         const int idx = tb / P;
@@ -1222,14 +1227,14 @@ __global__ __launch_bounds__(256) void part_narrow_kernel(const PartArgs a) {
         for (int nb = 0; nb < 2; ++nb) {
             const uint16_t *kp = a.k_pages + row(16 * nb + col) + CW * wave + 8 * grp;
 #pragma unroll
-            for (int kb = 0; kb < NKB; ++kb) kr[nb][kb] = *reinterpret_cast<const u32x4 *>(kp + 32 * kb);
+            for (int kb = 0; kb < NKB; ++kb) kr[nb][kb] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(kp + 32 * kb));
         }
 #pragma unroll
         for (int j = 0; j < KT / 4; ++j) {
             const int r = 4 * j + grp;
             const int piece = (lane & 15) ^ (2 * (r & 7));
             const char *src = reinterpret_cast<const char *>(a.v_pages + row(r) + CW * wave) + 16 * piece;
-            load_to_lds<false>(src, vb + 4 * j * 2 * CW);
+            load_to_lds<true>(src, vb + 4 * j * 2 * CW);
         }
     };
 
@@ -1463,8 +1468,7 @@ static hipError_t launch_dgq(const PartArgs &a, hipStream_t st) {
 
 template <int D, int G, int KS>
 static hipError_t launch_dg(const PartArgs &a, hipStream_t st) {
-    if constexpr (D == 128 || D == 256)
-        if (a.tiles == 1) return launch_dgq<D, G, 1, KS, true>(a, st);
+    if (a.tiles == 1) return launch_dgq<D, G, 1, KS, true>(a, st);
     return launch_dgq<D, G, 1, KS, false>(a, st);
 }
 
