@@ -93,9 +93,8 @@ hipError_t launch_rows_put(const RowsArgs &a, hipStream_t st) {
     return hipGetLastError();
 }
 
-// One wave per (stream, row, query head) and slice of CW channels: 128 at D = 128 with up to
-// 16 splits, else 64 (so that a lane walks few splits: a d 512 verify has about 100, a long
-// single-stream decode about 100 as well).  Lane = (split group sg, channel block cb):
+// One wave per (stream, row, query head) and slice of CW channels, CW chosen per call so that a
+// wave holds all of a row's splits in one pass where it can (launch_merge).  Lane = (split group sg, channel block cb):
 // it owns channels [8 cb, 8 cb + 8) of its slice for the splits i = sg, sg + SG, ...; the split
 // groups are summed at the end in a fixed order, so the result depends only on the partials,
 // not on timing.
@@ -234,17 +233,30 @@ __global__ __launch_bounds__(64) void merge_kernel(const MergeArgs a) {
 hipError_t launch_merge(const MergeArgs &a, hipStream_t st) {
     const int blocks = a.S * a.R * a.Hq;
     if (blocks == 0) return hipSuccess;
-    if (a.D == 128 && a.n_splits <= 16)
-        hipLaunchKernelGGL((merge_kernel<128, 128>), dim3(blocks), dim3(64), 0, st, a);
-    else if (a.D == 128)
-        hipLaunchKernelGGL((merge_kernel<128, 64>), dim3(blocks * 2), dim3(64), 0, st, a);
-    else if (a.D == 256)
-        hipLaunchKernelGGL((merge_kernel<256, 64>), dim3(blocks * 4), dim3(64), 0, st, a);
-    else if (a.D == 512)
-        hipLaunchKernelGGL((merge_kernel<512, 64>), dim3(blocks * 8), dim3(64), 0, st, a);
-    else
-        return hipErrorInvalidValue;
-    return hipGetLastError();
+    if (a.D != 128 && a.D != 256 && a.D != 512) return hipErrorInvalidValue;
+    // The widest channel slice whose wave holds every split of a row in one pass (4 per lane,
+    // 64 / (CW / 8) split groups: 2048 / CW splits), down to 32 channels; past 64 splits,
+    // 64-channel slices in several passes.  One pass with the loads issued before the
+    // stream's length is one round trip to memory: the 2,048-key d 512 decode (64 splits) in
+    // 32-channel slices, cold whole call 15.3-15.5 -> 14.5-14.8 us.  16-channel slices (2,048
+    // one-wave workgroups for the d 512 verify's 94 splits) measured slower than several
+    // passes over 64 channels: 27.8 against 26.0 us.
+    int cw = 64;
+    for (int c = 128; c >= 32; c /= 2)
+        if (c <= a.D && a.n_splits <= 2048 / c) {
+            cw = c;
+            break;
+        }
+#define KVP_MERGE(d, c)                                                                                  \
+    if (a.D == d && cw == c) {                                                                           \
+        hipLaunchKernelGGL((merge_kernel<d, c>), dim3(blocks * (d / c)), dim3(64), 0, st, a);            \
+        return hipGetLastError();                                                                        \
+    }
+    KVP_MERGE(128, 128) KVP_MERGE(128, 64) KVP_MERGE(128, 32)
+    KVP_MERGE(256, 128) KVP_MERGE(256, 64) KVP_MERGE(256, 32)
+    KVP_MERGE(512, 128) KVP_MERGE(512, 64) KVP_MERGE(512, 32)
+#undef KVP_MERGE
+    return hipErrorInvalidValue;
 }
 
 }  // namespace kvp
